@@ -1,0 +1,75 @@
+"""Attention over the selected blocks (oracle; test infrastructure only).
+
+[Fluxion-NL] Probleemstelling item 1: after top-k selection, attention runs
+over the selected KV blocks only.  [NOSA-DE] Methodik §1, "ED-DMA": the
+exponential belongs to the attention computation.
+
+Definition used (standard scaled dot-product attention restricted to a token
+set): for a query row q and the selected tokens t,
+    s_t = (q . k_t) * scale          (scale = 1/sqrt(d) unless given)
+    m   = max_t s_t,  l = sum_t exp(s_t - m)
+    out = sum_t exp(s_t - m) v_t / l,  lse = m + ln l
+computed in float64; out is rounded once to the storage dtype by the caller.
+An empty token set gives out = 0 and lse = -inf.
+
+The split-K merge states how partial results over disjoint token sets combine:
+    M = max_i m_i,  L = sum_i l_i exp(m_i - M),
+    out = sum_i o_i exp(m_i - M) / L,  lse = M + ln L,
+where o_i is the unnormalised sum_t exp(s_t - m_i) v_t of part i.
+"""
+from __future__ import annotations
+
+from typing import List, Tuple
+
+import numpy as np
+
+
+def selected_tokens(sel: np.ndarray, g: int, T: int) -> np.ndarray:
+    """Ascending token indices covered by the selected blocks (valid tokens only)."""
+    parts = [np.arange(j * g, min((j + 1) * g, T), dtype=np.int64) for j in np.asarray(sel)]
+    if not parts:
+        return np.zeros(0, dtype=np.int64)
+    return np.concatenate(parts)
+
+
+def attend(q_rows: np.ndarray, K_sel: np.ndarray, V_sel: np.ndarray, scale: float
+           ) -> Tuple[np.ndarray, np.ndarray]:
+    """(out [G][d], lse [G]) of the query rows over the given key/value rows, float64."""
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    G, d = q_rows.shape
+    if K_sel.shape[0] == 0:
+        return np.zeros((G, V_sel.shape[1])), np.full(G, -np.inf)
+    s = (q_rows @ np.asarray(K_sel, dtype=np.float64).T) * scale     # [G][n]
+    m = s.max(axis=1, keepdims=True)
+    p = np.exp(s - m)
+    l = p.sum(axis=1, keepdims=True)
+    out = (p @ np.asarray(V_sel, dtype=np.float64)) / l
+    lse = m[:, 0] + np.log(l[:, 0])
+    return out, lse
+
+
+def partial(q_rows: np.ndarray, K_part: np.ndarray, V_part: np.ndarray, scale: float
+            ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """Unnormalised partial (m [G], l [G], o [G][d]) over one part of the token set."""
+    q_rows = np.asarray(q_rows, dtype=np.float64)
+    G = q_rows.shape[0]
+    if K_part.shape[0] == 0:
+        return np.full(G, -np.inf), np.zeros(G), np.zeros((G, V_part.shape[1]))
+    s = (q_rows @ np.asarray(K_part, dtype=np.float64).T) * scale
+    m = s.max(axis=1)
+    p = np.exp(s - m[:, None])
+    return m, p.sum(axis=1), p @ np.asarray(V_part, dtype=np.float64)
+
+
+def merge_partials(parts: List[Tuple[np.ndarray, np.ndarray, np.ndarray]]
+                   ) -> Tuple[np.ndarray, np.ndarray]:
+    """Combine partials of disjoint token sets into (out, lse)."""
+    ms = np.stack([p[0] for p in parts])                # [n][G]
+    M = ms.max(axis=0)
+    if np.all(np.isneginf(M)):
+        G, d = parts[0][2].shape
+        return np.zeros((G, d)), np.full(G, -np.inf)
+    w = np.where(np.isneginf(ms), 0.0, np.exp(ms - M))  # [n][G]
+    L = sum(w[i] * parts[i][1] for i in range(len(parts)))
+    O = sum(w[i][:, None] * parts[i][2] for i in range(len(parts)))
+    return O / L[:, None], M + np.log(L)

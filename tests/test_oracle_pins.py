@@ -1,0 +1,74 @@
+"""The CPU oracle against its pins (no GPU)."""
+import numpy as np
+import pytest
+
+from oracle import attention, delta, numerics, pooling, scoring, selection
+from oracle.step import unit_step
+
+import oracle_pins as pins
+
+
+def test_bf16_rounding():
+    pins.check_bf16_rounding(numerics.f64_to_bf16_bits, numerics.round_f64_to_bf16)
+
+
+def test_pooling():
+    pins.check_pooling(pooling.block_summaries)
+
+
+def test_pooling_refuses_inexact_sums():
+    K = np.zeros((16, 2))
+    K[0, 0] = 1.0
+    K[1, 0] = 2.0 ** -40          # float32 values whose float64 sum would need > 53 bits
+    K[2, 0] = 2.0 ** 20
+    with pytest.raises(ValueError):
+        pooling.block_summaries(K, 16, 16, "f32")
+
+
+def test_scoring():
+    pins.check_scoring(scoring.block_scores)
+
+
+def test_forced_sets():
+    pins.check_forced(selection.forced_blocks)
+
+
+def test_budget():
+    pins.check_budget(selection.budget_k)
+
+
+def test_top_k():
+    pins.check_top_k(selection.top_k)
+
+
+def test_select_retrieval():
+    pins.check_select_retrieval(selection.select_unit)
+
+
+def test_select_nosa():
+    pins.check_select_nosa(selection.select_unit)
+
+
+def test_attention():
+    pins.check_attention(attention.attend, attention.selected_tokens,
+                         attention.merge_partials, attention.partial)
+
+
+def test_delta():
+    pins.check_delta(delta.selection_delta, delta.locality)
+
+
+def test_unit_step_dense_when_budget_covers_everything():
+    """End to end: budget >= all blocks, and block size 1 with k = n, are dense attention."""
+    rng = np.random.default_rng(20)
+    G, d, T = 2, 16, 100
+    q = pins.random_bf16_values(rng, (G, d))
+    K = pins.random_bf16_values(rng, (T, d))
+    V = pins.random_bf16_values(rng, (T, d))
+    scale = d ** -0.5
+    dense = pins._dense_masked(q, K, V, np.arange(T), scale)
+    for pol in (pins.Pol(mode=0, block=16, sub_block=4, top_k=1000),
+                pins.Pol(mode=0, block=1, sub_block=1, top_k=T)):
+        r = unit_step(pol, T, "bf16", q, K, V, scale)
+        assert list(r.sel) == list(range(-(-T // pol.block)))
+        assert np.allclose(r.out_exact, dense, rtol=1e-12, atol=1e-12)
