@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark one block-sparse decode step on one MI355X.
+
+A step is one pass of the whole hot path over one batch of synthetic input:
+  fx_build_summaries  (the newest full block of every unit, as when a block fills)
+  fx_select           (scores + per-kv-head selection)
+  fx_sparse_decode    (split-K attention over the selected blocks + merge)
+  fx_selection_delta  (against the previous step's selection)
+Inputs are resident in HBM before timing starts.  The default workload is the mixed
+serving batch (64 sequences of U{8192..131072} tokens, 32 q / 8 kv heads, d 128,
+bf16, block 64, streaming/retrieval kv heads), the largest of the five workloads.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "effective KV GB/s read (and µs) per sparse decode step, % of HBM peak"
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
+INT32_MAX = 2 ** 31 - 1
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes(w, max_sel, sel_idx, sel_cnt):
+    """The method's own HBM traffic for one step (split-K partials and scores excluded).
+
+    Per unit: KV = 2 d e N (N = valid tokens of the selected blocks); summaries read by
+    scoring = n_full d e (retrieval / NOSA units); newest-block summary build = g d e read
+    + d e write; NOSA logits n_full * 4 and mask words read + written.  Shared: q read by
+    select and decode, out written, lse written, selection indices written by select,
+    read by decode, read twice and written twice (padded) by the delta.
+    """
+    import numpy as np
+    e, d = w.elem_bytes, w.head_dim
+    parts = dict(kv=0, summaries=0, build=0, logits_mask=0, q=0, out=0, lse=0, indices=0)
+    n_q = w.batch * w.num_q_heads
+    tot_cnt = 0
+    for u in range(w.num_units):
+        b = u // w.num_kv_heads
+        p = w.policies[u]
+        T, g = w.seq_lens[b], p.block
+        n_full = T // g
+        cnt = int(sel_cnt[u])
+        tot_cnt += cnt
+        sel = sel_idx[u, :cnt].astype(np.int64)
+        N = int(np.minimum(g, T - sel * g).clip(min=0).sum())
+        parts["kv"] += 2 * d * e * N
+        if p.mode != 1:
+            parts["summaries"] += n_full * d * e
+        if n_full >= 1:
+            parts["build"] += g * d * e + d * e
+        if p.mode == 2:
+            parts["logits_mask"] += n_full * 4 + 2 * 4 * (-(-n_full // 32))
+    parts["q"] = 2 * n_q * d * e
+    parts["out"] = n_q * d * e
+    parts["lse"] = n_q * 4
+    parts["indices"] = (w.num_units * max_sel * 4) + tot_cnt * 4 + 2 * tot_cnt * 4 \
+        + 2 * w.num_units * max_sel * 4
+    total = sum(parts.values())
+    decode = parts["kv"] + n_q * d * e + parts["out"] + parts["lse"] + tot_cnt * 4
+    return total, decode, parts
+
+
+def cpu_baseline(w, inp, seconds: float, seed: int = 0):
+    """Time the oracle on a bounded sample of this workload's units, one step each."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle.delta import selection_delta
+    from oracle.pooling import block_summaries
+    from oracle.step import unit_step
+    from workloads import unit_arrays
+    from workloads.generate import unit_logits
+
+    scale = 1.0 / math.sqrt(w.head_dim)
+    order = np.random.default_rng(seed).permutation(w.num_units)
+    e, d, G = w.elem_bytes, w.head_dim, w.group
+    done, spent, nbytes = 0, 0.0, 0
+    with threadpool_limits(limits=1):
+        for u in order:
+            b, h = divmod(int(u), w.num_kv_heads)
+            p = w.policies[u]
+            T, g = w.seq_lens[b], p.block
+            q_rows, K, V = unit_arrays(inp, b, h)
+            logits = unit_logits(inp, int(u))
+            summ = block_summaries(K, p.block, p.sub_block, w.dtype)   # resident, not timed
+            n_full = T // g
+            t0 = time.perf_counter()
+            if n_full >= 1:
+                block_summaries(K[(n_full - 1) * g:n_full * g], g, p.sub_block, w.dtype)
+            r = unit_step(p, T, w.dtype, q_rows, K, V, scale, logits=logits, summaries=summ)
+            selection_delta(np.zeros(0, np.int64), r.sel)
+            spent += time.perf_counter() - t0
+            N = int(np.minimum(g, T - r.sel * g).clip(min=0).sum())
+            nbytes += 2 * d * e * N + (n_full * d * e if p.mode != 1 else 0) \
+                + (g * d * e + d * e if n_full else 0) + 3 * G * d * e + G * 4
+            done += 1
+            if spent >= seconds:
+                break
+    return {
+        "value": nbytes / spent / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+        "sample": f"{done} of {w.num_units} (sequence, kv head) units of {w.name}, one step each "
+                  f"(newest-block summary + scores + selection + attention + delta; the other "
+                  f"summaries precomputed as on the GPU), float64 NumPy, 1 thread; "
+                  f"{nbytes / 1e6:.1f} MB algorithmic in {spent:.2f} s",
+    }
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixed_serving")
+    ap.add_argument("--split", type=int, default=0, help="split-K chunk (tokens), 0 = plan default")
+    ap.add_argument("--flush", action="store_true",
+                    help="overwrite 1 GiB between steps (outside the timed events)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on exactly one GPU (asked for --gpus {args.gpus}); "
+              f"the path shards by (sequence, kv head) with no exchange, see DESIGN.md",
+              file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import block_sparse_decode_summary_amd as fx
+    from workloads import WORKLOAD_NAMES, generate, get_workload, query_at_step
+
+    if args.workload not in WORKLOAD_NAMES:
+        raise SystemExit(f"unknown workload {args.workload}; one of {WORKLOAD_NAMES}")
+    w = get_workload(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    inp = generate(w, dev)
+    torch.cuda.synchronize()
+    log(f"[bench] {w.name}: inputs generated in {time.time() - t0:.1f} s "
+        f"(K+V {2 * inp.K.numel() * inp.K.element_size() / 1e9:.1f} GB)")
+
+    dt = fx.FX_F32 if w.dtype == "f32" else fx.FX_BF16
+    plan = fx.fx_plan_create(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.t_cap, dt,
+                             list(w.policies), args.split)
+    A = fx.allocate_step_buffers(plan, dev)
+    Bsel = fx.allocate_step_buffers(plan, dev)     # second selection buffer for the delta
+    scale = 1.0 / math.sqrt(w.head_dim)
+    qs = [query_at_step(w, t, dev) for t in range(w.steps)] if w.drift else [inp.q]
+    logits = inp.logits
+    mask = A.evicted_mask if w.has_nosa else None
+    fx.fx_build_summaries(plan, inp.K, inp.seq_lens, 0, INT32_MAX, A.summaries)   # prefill
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if args.flush else None
+
+    cur, prev = A, Bsel
+
+    def step(i):
+        nonlocal cur, prev
+        q = qs[i % len(qs)]
+        fx.fx_build_summaries(plan, inp.K, inp.seq_lens, -1, INT32_MAX, A.summaries)
+        fx.fx_select(plan, q, A.summaries, logits, mask, inp.seq_lens, cur.sel_idx, cur.sel_cnt,
+                     A.workspace)
+        ev_d0[i].record()
+        fx.fx_sparse_decode(plan, q, inp.K, inp.V, inp.seq_lens, cur.sel_idx, cur.sel_cnt, scale,
+                            A.out, A.lse, A.workspace)
+        ev_d1[i].record()
+        fx.fx_selection_delta(plan, prev.sel_idx, prev.sel_cnt, cur.sel_idx, cur.sel_cnt,
+                              A.added, A.added_cnt, A.removed, A.removed_cnt)
+        cur, prev = prev, cur
+
+    n_ev = args.warmup + args.steps
+    mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    ev_s0, ev_s1, ev_d0, ev_d1 = mk(), mk(), mk(), mk()
+    for i in range(args.warmup):
+        ev_s0[i].record()
+        step(i)
+        ev_s1[i].record()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(args.warmup, n_ev):
+        if flush_buf is not None:
+            flush_buf.fill_(i & 0xFF)
+        ev_s0[i].record()
+        step(i)
+        ev_s1[i].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = [ev_s0[i].elapsed_time(ev_s1[i]) for i in range(args.warmup, n_ev)]
+    dec_ms = [ev_d0[i].elapsed_time(ev_d1[i]) for i in range(args.warmup, n_ev)]
+    ms_per_step = float(np.mean(step_ms))
+    dec_avg = float(np.mean(dec_ms))
+    if fx.fx_read_error(plan) != 0:
+        raise SystemExit("device error word set during the benchmark")
+
+    sel_idx = prev.sel_idx.cpu().numpy()      # the last step's selection
+    sel_cnt = prev.sel_cnt.cpu().numpy()
+    total_b, dec_b, parts = algorithmic_bytes(w, plan.max_selected, sel_idx, sel_cnt)
+    value = total_b / (ms_per_step * 1e-3) / 1e9
+    achieved = dec_b / (dec_avg * 1e-3) / 1e9
+    log(f"[bench] {w.name}: {ms_per_step * 1e3:.1f} us/step (p10 {np.percentile(step_ms, 10) * 1e3:.1f},"
+        f" p90 {np.percentile(step_ms, 90) * 1e3:.1f}), decode {dec_avg * 1e3:.1f} us; "
+        f"{total_b / 1e6:.1f} MB/step -> {value:.0f} GB/s ({100 * value / HBM_PEAK_GBS:.1f}% of peak); "
+        f"decode {achieved:.0f} GB/s; wall {wall / args.steps * 1e3:.3f} ms/step")
+    log(f"[bench] bytes/step: " + ", ".join(f"{k} {v / 1e6:.2f} MB" for k, v in parts.items()))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] timing the CPU oracle on a sample (~{args.cpu_seconds:.0f} s)")
+        cpu = cpu_baseline(w, inp, args.cpu_seconds)
+        log(f"[bench] oracle: {cpu['value']:.4f} GB/s ({cpu['sample']})")
+
+    shapes = {
+        "workload": w.name, "batch": w.batch, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+        "head_dim": w.head_dim, "t_cap": w.t_cap,
+        "seq_lens": "U{8192..131072}" if w.name == "mixed_serving" else w.seq_lens[0],
+        "blocks": sorted({p.block for p in w.policies}), "split_tokens": plan.split_tokens,
+        "cache_flush_between_steps": bool(args.flush),
+    }
+    line = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "us_per_step": round(ms_per_step * 1e3, 2),
+        "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic (seeded; shapes and value distributions of the workload definition)",
+        "config": shapes,
+        "alg_bytes_per_step": int(total_b),
+        "roofline": {"bound": "hbm", "kernel": "k_decode (fx_sparse_decode)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "alg_bytes_per_launch": int(dec_b), "avg_launch_us": round(dec_avg * 1e3, 2)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,317 @@
+// libfx host side: plan creation, argument validation, workspace layout, entry points.
+//
+// Everything here runs on the host.  Validation happens before any HIP call, so the
+// error paths work (and are tested) on machines without a GPU.  No C++ exception
+// leaves this file: every entry point catches and maps to a status.
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <cstring>
+#include <new>
+
+#include "fx_internal.h"
+
+namespace {
+
+using fx::UnitInfo;
+
+bool is_pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+int log2i(int64_t x) {
+  int r = 0;
+  while ((int64_t(1) << r) < x) ++r;
+  return r;
+}
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+bool req(const void* p, size_t a) { return p != nullptr && aligned(p, a); }
+bool opt(const void* p, size_t a) { return p == nullptr || aligned(p, a); }
+
+fx_status check_desc(const fx_plan_desc* d) {
+  if (!d) return FX_E_INVALID;
+  if (d->batch < 1 || d->num_kv_heads < 1 || d->num_q_heads < 1) return FX_E_INVALID;
+  if (d->num_q_heads % d->num_kv_heads != 0) return FX_E_INVALID;
+  const int G = d->num_q_heads / d->num_kv_heads;
+  if (G < 1 || G > fx::kMaxGroup) return FX_E_INVALID;
+  if (d->head_dim != 64 && d->head_dim != 128) return FX_E_INVALID;
+  if (d->t_cap < 1 || d->t_cap > fx::kMaxTcap) return FX_E_INVALID;
+  if (d->dtype != FX_F32 && d->dtype != FX_BF16) return FX_E_INVALID;
+  if (d->split_tokens != 0 &&
+      (!is_pow2(d->split_tokens) || d->split_tokens < fx::kMinSplit ||
+       d->split_tokens > fx::kMaxSplit))
+    return FX_E_INVALID;
+  if ((int64_t)d->batch * d->num_kv_heads > (1 << 20)) return FX_E_INVALID;
+  return FX_OK;
+}
+
+fx_status check_policy(const fx_head_policy& p) {
+  if (p.mode != FX_RETRIEVAL && p.mode != FX_STREAMING && p.mode != FX_NOSA) return FX_E_INVALID;
+  if (!is_pow2(p.block) || p.block > fx::kMaxBlock) return FX_E_INVALID;
+  if (!is_pow2(p.sub_block) || p.sub_block > p.block) return FX_E_INVALID;
+  if ((p.force_sink != 0 && p.force_sink != 1) || (p.force_last != 0 && p.force_last != 1))
+    return FX_E_INVALID;
+  switch (p.mode) {
+    case FX_RETRIEVAL:
+      if (p.top_k < 0) return FX_E_INVALID;
+      if (p.top_k == 0 && !(p.budget > 0.0f && p.budget <= 1.0f)) return FX_E_INVALID;
+      break;
+    case FX_STREAMING:
+      if (p.sink_tokens < 0 || p.local_tokens < 0) return FX_E_INVALID;
+      break;
+    case FX_NOSA:
+      if (p.top_k < 0 || p.k_evict < 0 || (int64_t)p.top_k + p.k_evict < 1) return FX_E_INVALID;
+      break;
+  }
+  return FX_OK;
+}
+
+// Largest selection a unit can produce for any seq_len <= t_cap.
+int64_t max_selected(const fx_head_policy& p, int64_t n_cap) {
+  int64_t m;
+  switch (p.mode) {
+    case FX_STREAMING:
+      m = ceil_div(p.sink_tokens, p.block) + ceil_div(p.local_tokens, p.block) + 2;
+      break;
+    case FX_RETRIEVAL: {
+      const int64_t k = p.top_k > 0 ? p.top_k
+                                    : (int64_t)std::ceil((double)p.budget * (double)n_cap);
+      m = k + 2;
+      break;
+    }
+    default:
+      m = (int64_t)p.top_k + p.k_evict + 2;
+  }
+  return std::min(m, n_cap);
+}
+
+fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_plan_t* out) {
+  if (!out) return FX_E_INVALID;
+  fx_status st = check_desc(desc);
+  if (st != FX_OK) return st;
+  if (!pol) return FX_E_INVALID;
+  const int units = desc->batch * desc->num_kv_heads;
+  for (int u = 0; u < units; ++u) {
+    st = check_policy(pol[u]);
+    if (st != FX_OK) return st;
+  }
+
+  fx_plan* p = new (std::nothrow) fx_plan();
+  if (!p) return FX_E_HIP;
+  p->desc = *desc;
+  p->G = desc->num_q_heads / desc->num_kv_heads;
+  p->units = units;
+  p->host_units.resize(units);
+  int64_t boff = 0, moff = 0, max_sel = 1, max_ncap = 0, max_nfull = 0, work = 0, max_tok = 1;
+  for (int u = 0; u < units; ++u) {
+    const fx_head_policy& q = pol[u];
+    UnitInfo& ui = p->host_units[u];
+    const int64_t n_cap = ceil_div(desc->t_cap, q.block);
+    ui.mode = q.mode;
+    ui.g = q.block;
+    ui.log2g = log2i(q.block);
+    ui.s = q.sub_block;
+    ui.top_k = q.top_k;
+    ui.budget = q.budget;
+    ui.k_evict = q.k_evict;
+    ui.sink = q.sink_tokens;
+    ui.local = q.local_tokens;
+    ui.force_sink = q.force_sink;
+    ui.force_last = q.force_last;
+    const int64_t ms = max_selected(q, n_cap);
+    ui.max_sel = (int32_t)ms;
+    ui.n_cap = (int32_t)n_cap;
+    ui.mask_off = (int32_t)moff;
+    ui.block_off = boff;
+    boff += n_cap;
+    moff += ceil_div(n_cap, 32);
+    max_sel = std::max(max_sel, ms);
+    max_ncap = std::max(max_ncap, n_cap);
+    max_nfull = std::max<int64_t>(max_nfull, desc->t_cap / q.block);
+    const int64_t tok = std::min<int64_t>(ms * q.block, desc->t_cap);
+    work += tok;
+    max_tok = std::max(max_tok, tok);
+    if (q.mode != FX_STREAMING) p->any_scored = true;
+    if (q.mode == FX_NOSA && q.k_evict > 0) p->needs_logits = true;
+  }
+  if (moff > INT32_MAX || max_sel > INT32_MAX / 2) {
+    delete p;
+    return FX_E_UNSUPPORTED;
+  }
+  p->total_blocks = boff;
+  p->mask_words = moff;
+  p->max_sel = (int32_t)max_sel;
+  p->max_n_cap = (int32_t)max_ncap;
+  p->max_n_full_cap = (int32_t)max_nfull;
+
+  int64_t split = desc->split_tokens;
+  if (split == 0) {
+    split = 256;
+    while (split < 1024 && split * 2 * 4096 <= work) split *= 2;
+  }
+  p->split = (int32_t)split;
+  p->log2split = log2i(split);
+  p->max_chunks = (int32_t)ceil_div(max_tok, split);
+
+  const int d = desc->head_dim;
+  size_t off = 0;
+  p->ws_scores_off = off;
+  off += align_up((size_t)(p->any_scored ? p->total_blocks : 0) * 4, 256);
+  p->ws_part_o_off = off;
+  off += align_up((size_t)units * p->max_chunks * p->G * d * 4, 256);
+  p->ws_part_ml_off = off;
+  off += align_up((size_t)units * p->max_chunks * p->G * 8, 256);
+  p->ws_total = std::max<size_t>(off, 256);
+
+  // Device table: units | counters | error word.
+  const size_t tab_units = align_up(sizeof(UnitInfo) * units, 256);
+  const size_t tab_cnt = align_up(sizeof(int32_t) * units, 256);
+  const size_t tab_bytes = tab_units + tab_cnt + 256;
+  if (hipGetDevice(&p->device) != hipSuccess ||
+      hipMalloc(&p->d_table, tab_bytes) != hipSuccess) {
+    delete p;
+    return FX_E_HIP;
+  }
+  char* base = static_cast<char*>(p->d_table);
+  p->d_units = reinterpret_cast<UnitInfo*>(base);
+  p->d_counters = reinterpret_cast<int32_t*>(base + tab_units);
+  p->d_error = reinterpret_cast<uint32_t*>(base + tab_units + tab_cnt);
+  if (hipMemcpy(p->d_units, p->host_units.data(), sizeof(UnitInfo) * units,
+                hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemset(base + tab_units, 0, tab_cnt + 256) != hipSuccess) {
+    (void)hipFree(p->d_table);
+    delete p;
+    return FX_E_HIP;
+  }
+  *out = p;
+  return FX_OK;
+}
+
+fx_status hip_status(hipError_t e) { return e == hipSuccess ? FX_OK : FX_E_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+fx_status fx_plan_create(const fx_plan_desc* desc, const fx_head_policy* host_policies,
+                         fx_plan_t* out) {
+  try {
+    return plan_create(desc, host_policies, out);
+  } catch (...) {
+    return FX_E_HIP;
+  }
+}
+
+fx_status fx_plan_destroy(fx_plan_t plan) {
+  if (!plan) return FX_OK;
+  fx_status st = FX_OK;
+  if (plan->d_table && hipFree(plan->d_table) != hipSuccess) st = FX_E_HIP;
+  delete plan;
+  return st;
+}
+
+size_t fx_summary_bytes(fx_plan_t p) {
+  if (!p) return 0;
+  return (size_t)p->total_blocks * p->desc.head_dim * (p->desc.dtype == FX_BF16 ? 2 : 4);
+}
+size_t fx_logits_bytes(fx_plan_t p) { return p ? (size_t)p->total_blocks * 4 : 0; }
+size_t fx_evict_mask_bytes(fx_plan_t p) { return p ? (size_t)p->mask_words * 4 : 0; }
+size_t fx_workspace_bytes(fx_plan_t p) { return p ? p->ws_total : 0; }
+int32_t fx_max_selected(fx_plan_t p) { return p ? p->max_sel : -1; }
+int32_t fx_split_tokens(fx_plan_t p) { return p ? p->split : -1; }
+int64_t fx_unit_block_offset(fx_plan_t p, int32_t unit) {
+  if (!p || unit < 0 || unit >= p->units) return -1;
+  return p->host_units[unit].block_off;
+}
+
+const char* fx_status_string(fx_status s) {
+  switch (s) {
+    case FX_OK: return "FX_OK";
+    case FX_E_INVALID: return "FX_E_INVALID: an argument or policy is out of range, null or misaligned";
+    case FX_E_UNSUPPORTED: return "FX_E_UNSUPPORTED: no kernel for this request";
+    case FX_E_WORKSPACE: return "FX_E_WORKSPACE: workspace smaller than fx_workspace_bytes()";
+    case FX_E_HIP: return "FX_E_HIP: a HIP runtime call or kernel launch failed";
+  }
+  return "unknown fx_status";
+}
+
+fx_status fx_read_error(fx_plan_t p, uint32_t* host_word) {
+  if (!p || !host_word) return FX_E_INVALID;
+  if (hipDeviceSynchronize() != hipSuccess) return FX_E_HIP;
+  if (hipMemcpy(host_word, p->d_error, 4, hipMemcpyDeviceToHost) != hipSuccess) return FX_E_HIP;
+  if (hipMemset(p->d_error, 0, 4) != hipSuccess) return FX_E_HIP;
+  return FX_OK;
+}
+
+fx_status fx_build_summaries(fx_plan_t p, const void* K, const int32_t* seq_lens,
+                             int32_t block_begin, int32_t block_end, void* summaries,
+                             hipStream_t stream) {
+  if (!p || !req(K, 16) || !req(seq_lens, 4) || !req(summaries, 16)) return FX_E_INVALID;
+  try {
+    return hip_status(
+        fx::launch_build_summaries(p, K, seq_lens, block_begin, block_end, summaries, stream));
+  } catch (...) {
+    return FX_E_HIP;
+  }
+}
+
+fx_status fx_select(fx_plan_t p, const void* q, const void* summaries, const float* evict_logits,
+                    uint32_t* evicted_mask, const int32_t* seq_lens, int32_t* sel_idx,
+                    int32_t* sel_cnt, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+  if (!p || !req(q, 16) || !req(seq_lens, 4) || !req(sel_idx, 4) || !req(sel_cnt, 4) ||
+      !req(workspace, 16))
+    return FX_E_INVALID;
+  if (p->any_scored && !req(summaries, 16)) return FX_E_INVALID;
+  if (!opt(evict_logits, 4) || !opt(evicted_mask, 4)) return FX_E_INVALID;
+  if (p->needs_logits && (!evict_logits || !evicted_mask)) return FX_E_INVALID;
+  if (workspace_bytes < p->ws_total) return FX_E_WORKSPACE;
+  try {
+    float* scores = reinterpret_cast<float*>(static_cast<char*>(workspace) + p->ws_scores_off);
+    if (p->any_scored) {
+      hipError_t e = fx::launch_score(p, q, summaries, seq_lens, scores, stream);
+      if (e != hipSuccess) return FX_E_HIP;
+    }
+    return hip_status(fx::launch_topk(p, scores, evict_logits, evicted_mask, seq_lens, sel_idx,
+                                      sel_cnt, stream));
+  } catch (...) {
+    return FX_E_HIP;
+  }
+}
+
+fx_status fx_sparse_decode(fx_plan_t p, const void* q, const void* K, const void* V,
+                           const int32_t* seq_lens, const int32_t* sel_idx,
+                           const int32_t* sel_cnt, float softmax_scale, void* out, float* lse,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!p || !req(q, 16) || !req(K, 16) || !req(V, 16) || !req(seq_lens, 4) ||
+      !req(sel_idx, 4) || !req(sel_cnt, 4) || !req(out, 16) || !opt(lse, 4) ||
+      !req(workspace, 16))
+    return FX_E_INVALID;
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return FX_E_INVALID;
+  if (workspace_bytes < p->ws_total) return FX_E_WORKSPACE;
+  try {
+    char* ws = static_cast<char*>(workspace);
+    return hip_status(fx::launch_decode(p, q, K, V, seq_lens, sel_idx, sel_cnt, softmax_scale, out,
+                                        lse, reinterpret_cast<float*>(ws + p->ws_part_o_off),
+                                        reinterpret_cast<float*>(ws + p->ws_part_ml_off), stream));
+  } catch (...) {
+    return FX_E_HIP;
+  }
+}
+
+fx_status fx_selection_delta(fx_plan_t p, const int32_t* prev_idx, const int32_t* prev_cnt,
+                             const int32_t* cur_idx, const int32_t* cur_cnt, int32_t* added,
+                             int32_t* added_cnt, int32_t* removed, int32_t* removed_cnt,
+                             hipStream_t stream) {
+  if (!p || !req(prev_idx, 4) || !req(prev_cnt, 4) || !req(cur_idx, 4) || !req(cur_cnt, 4) ||
+      !req(added, 4) || !req(added_cnt, 4) || !req(removed, 4) || !req(removed_cnt, 4))
+    return FX_E_INVALID;
+  try {
+    return hip_status(fx::launch_delta(p, prev_idx, prev_cnt, cur_idx, cur_cnt, added, added_cnt,
+                                       removed, removed_cnt, stream));
+  } catch (...) {
+    return FX_E_HIP;
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,93 @@
+// Internal declarations shared by the host code and the kernel launchers of libfx.
+// Not part of the ABI (include/fx.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <vector>
+
+#include "fx.h"
+
+namespace fx {
+
+constexpr int kMaxGroup = 8;          // G = Hq / Hkv
+constexpr int kMaxBlock = 256;        // largest block size g
+constexpr int kMaxSplit = 2048;       // largest split-K chunk (tokens)
+constexpr int kMinSplit = 64;
+constexpr int kMaxTcap = 1 << 24;
+
+// Per-unit policy as the kernels read it (device table owned by the plan).
+struct UnitInfo {
+  int32_t mode;
+  int32_t g;           // block size
+  int32_t log2g;
+  int32_t s;           // sub-block size
+  int32_t top_k;
+  float budget;
+  int32_t k_evict;
+  int32_t sink;
+  int32_t local;
+  int32_t force_sink;
+  int32_t force_last;
+  int32_t max_sel;     // upper bound on this unit's selection size
+  int32_t n_cap;       // ceil(t_cap / g)
+  int32_t mask_off;    // first eviction-mask word of the unit
+  int64_t block_off;   // first block slot of the unit in the packed per-block arrays
+};
+static_assert(sizeof(UnitInfo) == 64, "UnitInfo is read as one 64-byte record");
+
+}  // namespace fx
+
+struct fx_plan {
+  fx_plan_desc desc;
+  int32_t G = 0;
+  int32_t units = 0;
+  std::vector<fx::UnitInfo> host_units;
+  int device = 0;
+  // device table: [units] UnitInfo | [units] int32 split-K counters | uint32 error word
+  void* d_table = nullptr;
+  fx::UnitInfo* d_units = nullptr;
+  int32_t* d_counters = nullptr;
+  uint32_t* d_error = nullptr;
+
+  int64_t total_blocks = 0;
+  int64_t mask_words = 0;
+  int32_t max_sel = 0;
+  int32_t max_n_cap = 0;
+  int32_t max_n_full_cap = 0;    // max over units of t_cap / g
+  int32_t split = 0;             // split-K chunk in tokens (power of two)
+  int32_t log2split = 0;
+  int32_t max_chunks = 0;        // chunks per unit, upper bound
+  bool any_scored = false;       // some unit is retrieval or NOSA
+  bool needs_logits = false;     // some NOSA unit has k_evict > 0
+
+  // workspace layout (byte offsets)
+  size_t ws_scores_off = 0;      // float [total_blocks]
+  size_t ws_part_o_off = 0;      // float [units][max_chunks][G][d]
+  size_t ws_part_ml_off = 0;     // float2 [units][max_chunks][G]  (m, l)
+  size_t ws_total = 0;
+};
+
+namespace fx {
+
+// Kernel launchers (one per .hip file).  They assume validated arguments.
+hipError_t launch_build_summaries(const fx_plan* p, const void* K, const int32_t* seq_lens,
+                                  int32_t block_begin, int32_t block_end, void* summaries,
+                                  hipStream_t stream);
+hipError_t launch_score(const fx_plan* p, const void* q, const void* summaries,
+                        const int32_t* seq_lens, float* scores, hipStream_t stream);
+hipError_t launch_topk(const fx_plan* p, const float* scores, const float* logits,
+                       uint32_t* mask, const int32_t* seq_lens, int32_t* sel_idx,
+                       int32_t* sel_cnt, hipStream_t stream);
+hipError_t launch_decode(const fx_plan* p, const void* q, const void* K, const void* V,
+                         const int32_t* seq_lens, const int32_t* sel_idx,
+                         const int32_t* sel_cnt, float softmax_scale, void* out, float* lse,
+                         float* part_o, float* part_ml, hipStream_t stream);
+hipError_t launch_delta(const fx_plan* p, const int32_t* prev_idx, const int32_t* prev_cnt,
+                        const int32_t* cur_idx, const int32_t* cur_cnt, int32_t* added,
+                        int32_t* added_cnt, int32_t* removed, int32_t* removed_cnt,
+                        hipStream_t stream);
+
+}  // namespace fx

@@ -1,0 +1,368 @@
+// Split-K flash-decoding over the selected blocks, with the chunk merge fused in.
+//
+// [Fluxion-NL] "Technische Samenvatting: Fluxion", Probleemstelling item 1: after
+// top-k block selection, attention runs over the selected KV blocks only; Kerninzichten
+// item 3: this work is bound by data movement, not arithmetic.  [NOSA-DE]
+// "Technisches Resümee: NOSA: Native und Offloadable Sparse Attention", Methodik §1,
+// "ED-DMA": the exponential belongs to the attention phase.
+//
+// Per unit (sequence b, kv head h) and query row q of its group:
+//   s_t = scale * (q . K_t) over the valid tokens t of the selected blocks,
+//   out = sum_t e^{s_t - m} V_t / l,  l = sum_t e^{s_t - m},  lse = m + ln l.
+// The selected tokens of a unit are numbered i = 0 .. N-1 in ascending order; because
+// only the last block of a unit can be partial and selections are ascending, token i
+// lives in selected block i / g at offset i % g.  Chunks of `split` tokens are one
+// workgroup each (grid = units x max_chunks; chunks past the unit's N exit at once).
+//
+// Inside a workgroup (4 waves), a token's d-vector is spread over LPT lanes, each lane
+// holding 16 bytes (8 bfloat16 / 4 float32) of the K and V rows: every load is a
+// 128-bit load and each wave instruction reads 64 x 16 contiguous bytes per 64/LPT
+// tokens.  Each lane keeps the G query rows' matching 16 bytes in registers, forms G
+// partial dot products (v_dot2_f32_bf16 for bfloat16), and DPP-reduces them across its
+// LPT lanes.  The online softmax runs in base 2 (scores pre-multiplied by
+// scale*log2(e)) per lane group; U tokens per lane group per step amortise the rescale.
+// Lane groups, then waves, merge with the log-sum-exp rule; a unit with one chunk
+// writes `out` directly.  Otherwise each chunk writes (o, m, l) to the workspace and
+// bumps the unit's counter; the last chunk to arrive merges all chunks in chunk order
+// (so the result does not depend on scheduling) and resets the counter.
+#include "fx_device.h"
+
+namespace fx {
+namespace {
+
+constexpr int NT = 256;
+constexpr int NWAVES = NT / 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegBig = -1.0e30f;   // running max before any token (finite: no inf - inf)
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+template <typename E>
+struct Lanes;
+template <>
+struct Lanes<bf16_t> {
+  static constexpr int EPL = 8;   // elements per lane per row (16 bytes)
+};
+template <>
+struct Lanes<float> {
+  static constexpr int EPL = 4;
+};
+
+// Partial dot product of this lane's 16 bytes of K with one query row's 16 bytes.
+__device__ __forceinline__ float lane_dot(const uint4& qv, const uint4& kv, bf16_t*) {
+  float acc = 0.0f;
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qv.x),
+                                        __builtin_bit_cast(bf16x2_t, kv.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qv.y),
+                                        __builtin_bit_cast(bf16x2_t, kv.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qv.z),
+                                        __builtin_bit_cast(bf16x2_t, kv.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, qv.w),
+                                        __builtin_bit_cast(bf16x2_t, kv.w), acc, false);
+  return acc;
+}
+__device__ __forceinline__ float lane_dot(const uint4& qv, const uint4& kv, float*) {
+  float acc = __uint_as_float(qv.x) * __uint_as_float(kv.x);
+  acc = fmaf(__uint_as_float(qv.y), __uint_as_float(kv.y), acc);
+  acc = fmaf(__uint_as_float(qv.z), __uint_as_float(kv.z), acc);
+  acc = fmaf(__uint_as_float(qv.w), __uint_as_float(kv.w), acc);
+  return acc;
+}
+
+__device__ __forceinline__ void unpack(const uint4& v, float* f, bf16_t*) {
+  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
+  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
+  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
+  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
+}
+__device__ __forceinline__ void unpack(const uint4& v, float* f, float*) {
+  f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
+  f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
+}
+
+template <typename E, int D, int G>
+struct DecodeLds {
+  static constexpr int EPL = Lanes<E>::EPL;
+  int blk[kMaxSplit + 1];          // selected block indices covering this chunk
+  float o[NWAVES][G][D];
+  float m[NWAVES][G];
+  float l[NWAVES][G];
+  int last;
+};
+
+template <typename E, int D, int G, int U>
+__global__ __launch_bounds__(NT) void k_decode(
+    const UnitInfo* __restrict__ units, const E* __restrict__ q, const E* __restrict__ K,
+    const E* __restrict__ V, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ sel_cnt, float scale_log2,
+    E* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
+    float2* __restrict__ part_ml, int32_t* __restrict__ counters, uint32_t* __restrict__ err,
+    int Hkv, int t_cap, int max_sel, int split, int log2split, int max_chunks) {
+  constexpr int EPL = Lanes<E>::EPL;
+  constexpr int LPT = D / EPL;        // lanes per token
+  constexpr int TPW = 64 / LPT;       // tokens per wave instruction
+  static_assert(LPT >= 4 && LPT <= 32 && 64 % LPT == 0, "lane layout");
+  __shared__ DecodeLds<E, D, G> L;
+
+  const int u = blockIdx.x / max_chunks;
+  const int chunk = blockIdx.x % max_chunks;
+  const UnitInfo ui = units[u];
+  const int b = u / Hkv, h = u % Hkv;
+  const int T = load_seq_len(seq_lens, b, t_cap, err);
+  const int g = ui.g, log2g = ui.log2g;
+
+  int cnt = sel_cnt[u];
+  if (cnt < 0 || cnt > max_sel) {
+    if (threadIdx.x == 0) atomicOr(err, (uint32_t)FX_ERR_SEL_COUNT);
+    cnt = cnt < 0 ? 0 : max_sel;
+  }
+  const int32_t* sel = sel_idx + (size_t)u * max_sel;
+  int N = 0;
+  if (cnt > 0) {
+    const int last = sel[cnt - 1];
+    const int valid_last = min(max(T - last * g, 0), g);
+    N = (cnt - 1) * g + valid_last;
+  }
+  if (N > max_chunks * split) {   // only for selections that are not valid for this unit
+    if (threadIdx.x == 0) atomicOr(err, (uint32_t)FX_ERR_SEL_INDEX);
+    N = max_chunks * split;
+  }
+  const int nchunks = N > 0 ? ((N + split - 1) >> log2split) : 1;
+  if (chunk >= nchunks) return;
+
+  const int i0 = chunk << log2split;
+  const int i1 = min(N, i0 + split);
+  // Block indices this chunk touches.
+  const int p0 = i0 >> log2g;
+  const int np = i1 > i0 ? ((i1 - 1) >> log2g) - p0 + 1 : 0;
+  for (int i = threadIdx.x; i < np; i += NT) {
+    const int jb = sel[p0 + i];
+    const bool ok = jb >= 0 && (int64_t)jb * g < T && (p0 + i == 0 || sel[p0 + i - 1] < jb);
+    if (!ok) atomicOr(err, (uint32_t)FX_ERR_SEL_INDEX);
+    L.blk[i] = ok ? jb : -1;
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lg = lane / LPT, li = lane % LPT;
+
+  // Query slices: this lane's 16 bytes of each of the G rows.
+  const size_t unit_rows = (size_t)u * t_cap;
+  const E* qrow = q + ((size_t)b * Hkv * G + (size_t)h * G) * D + li * EPL;
+  uint4 qv[G];
+#pragma unroll
+  for (int gg = 0; gg < G; ++gg) qv[gg] = *reinterpret_cast<const uint4*>(qrow + (size_t)gg * D);
+
+  float m[G], l[G], o[G][EPL];
+#pragma unroll
+  for (int gg = 0; gg < G; ++gg) {
+    m[gg] = kNegBig;
+    l[gg] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[gg][e] = 0.0f;
+  }
+
+  // This wave's share of the chunk.
+  const int per_wave = split / NWAVES;
+  const int w0 = i0 + wave * per_wave;
+  const int w1 = min(i1, w0 + per_wave);
+  const E* Kb = K + unit_rows * D + li * EPL;
+  const E* Vb = V + unit_rows * D + li * EPL;
+
+  for (int base = w0; base < w1; base += TPW * U) {
+    uint4 kr[U], vr[U];
+    bool ok[U];
+#pragma unroll
+    for (int uu = 0; uu < U; ++uu) {
+      const int i = base + uu * TPW + lg;
+      int row = -1;
+      if (i < w1) {
+        const int jb = L.blk[(i >> log2g) - p0];
+        row = jb * g + (i & (g - 1));
+      }
+      ok[uu] = row >= 0 && row < T;
+      if (ok[uu]) {
+        kr[uu] = *reinterpret_cast<const uint4*>(Kb + (size_t)row * D);
+        vr[uu] = *reinterpret_cast<const uint4*>(Vb + (size_t)row * D);
+      } else {
+        kr[uu] = make_uint4(0, 0, 0, 0);
+        vr[uu] = make_uint4(0, 0, 0, 0);
+      }
+    }
+    float s[U][G];
+#pragma unroll
+    for (int uu = 0; uu < U; ++uu)
+#pragma unroll
+      for (int gg = 0; gg < G; ++gg) s[uu][gg] = lane_dot(qv[gg], kr[uu], (E*)nullptr);
+#pragma unroll
+    for (int uu = 0; uu < U; ++uu)
+#pragma unroll
+      for (int gg = 0; gg < G; ++gg) {
+        const float t = group_sum<LPT>(s[uu][gg]) * scale_log2;
+        s[uu][gg] = ok[uu] ? t : -__builtin_inff();
+      }
+    float vf[U][EPL];
+#pragma unroll
+    for (int uu = 0; uu < U; ++uu) unpack(vr[uu], vf[uu], (E*)nullptr);
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) {
+      float mx = m[gg];
+#pragma unroll
+      for (int uu = 0; uu < U; ++uu) mx = fmaxf(mx, s[uu][gg]);
+      const float alpha = __builtin_amdgcn_exp2f(m[gg] - mx);
+      m[gg] = mx;
+      float lsum = l[gg] * alpha;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[gg][e] *= alpha;
+#pragma unroll
+      for (int uu = 0; uu < U; ++uu) {
+        const float p = __builtin_amdgcn_exp2f(s[uu][gg] - mx);
+        lsum += p;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[gg][e] = fmaf(p, vf[uu][e], o[gg][e]);
+      }
+      l[gg] = lsum;
+    }
+  }
+
+  // Merge the lane groups of the wave (partners differ in the lane bits above LPT).
+#pragma unroll
+  for (int off = LPT; off < 64; off <<= 1) {
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) {
+      const float m2 = __shfl_xor(m[gg], off);
+      const float l2 = __shfl_xor(l[gg], off);
+      const float M = fmaxf(m[gg], m2);
+      const float a = __builtin_amdgcn_exp2f(m[gg] - M);
+      const float c = __builtin_amdgcn_exp2f(m2 - M);
+      l[gg] = l[gg] * a + l2 * c;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        const float o2 = __shfl_xor(o[gg][e], off);
+        o[gg][e] = o[gg][e] * a + o2 * c;
+      }
+      m[gg] = M;
+    }
+  }
+  if (lg == 0) {
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) {
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) L.o[wave][gg][li * EPL + e] = o[gg][e];
+      if (li == 0) {
+        L.m[wave][gg] = m[gg];
+        L.l[wave][gg] = l[gg];
+      }
+    }
+  }
+  __syncthreads();
+
+  // Merge the waves in wave order; then either finish the unit or publish a partial.
+  const bool single = nchunks == 1;
+  const size_t pbase = (size_t)u * max_chunks + chunk;
+  for (int idx = threadIdx.x; idx < G * D; idx += NT) {
+    const int gg = idx / D, c = idx % D;
+    float M = L.m[0][gg];
+#pragma unroll
+    for (int w = 1; w < NWAVES; ++w) M = fmaxf(M, L.m[w][gg]);
+    float Ls = 0.0f, Os = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NWAVES; ++w) {
+      const float a = __builtin_amdgcn_exp2f(L.m[w][gg] - M);
+      Ls = fmaf(L.l[w][gg], a, Ls);
+      Os = fmaf(L.o[w][gg][c], a, Os);
+    }
+    if (single) {
+      const size_t orow = (size_t)b * Hkv * G + (size_t)h * G + gg;
+      store_elem(out + orow * D + c, Ls > 0.0f ? Os / Ls : 0.0f);
+      if (lse && c == 0) lse[orow] = Ls > 0.0f ? (M + __log2f(Ls)) * kLn2 : -__builtin_inff();
+    } else {
+      part_o[(pbase * G + gg) * D + c] = Os;
+      if (c == 0) part_ml[pbase * G + gg] = make_float2(M, Ls);
+    }
+  }
+  if (single) return;
+
+  // Last-arriver merge.  Release: make this chunk's partial visible device-wide
+  // (agent-scope fence writes back this XCD's L2) before counting it.
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int prev = atomicAdd(&counters[u], 1);
+    L.last = prev == nchunks - 1;
+  }
+  __syncthreads();
+  if (!L.last) return;
+  __threadfence();   // acquire: see every other chunk's partial
+  const size_t ubase = (size_t)u * max_chunks;
+  for (int idx = threadIdx.x; idx < G * D; idx += NT) {
+    const int gg = idx / D, c = idx % D;
+    float M = kNegBig;
+    for (int k = 0; k < nchunks; ++k) M = fmaxf(M, part_ml[(ubase + k) * G + gg].x);
+    float Ls = 0.0f, Os = 0.0f;
+    for (int k = 0; k < nchunks; ++k) {
+      const float2 ml = part_ml[(ubase + k) * G + gg];
+      const float a = __builtin_amdgcn_exp2f(ml.x - M);
+      Ls = fmaf(ml.y, a, Ls);
+      Os = fmaf(part_o[((ubase + k) * G + gg) * D + c], a, Os);
+    }
+    const size_t orow = (size_t)b * Hkv * G + (size_t)h * G + gg;
+    store_elem(out + orow * D + c, Ls > 0.0f ? Os / Ls : 0.0f);
+    if (lse && c == 0) lse[orow] = Ls > 0.0f ? (M + __log2f(Ls)) * kLn2 : -__builtin_inff();
+  }
+  if (threadIdx.x == 0) counters[u] = 0;
+}
+
+template <typename E, int D, int G>
+hipError_t launch_t(const fx_plan* p, const void* q, const void* K, const void* V,
+                    const int32_t* seq_lens, const int32_t* sel_idx, const int32_t* sel_cnt,
+                    float softmax_scale, void* out, float* lse, float* part_o, float* part_ml,
+                    hipStream_t stream) {
+  constexpr int U = 4;
+  const dim3 grid((unsigned)((int64_t)p->units * p->max_chunks));
+  k_decode<E, D, G, U><<<grid, NT, 0, stream>>>(
+      p->d_units, static_cast<const E*>(q), static_cast<const E*>(K), static_cast<const E*>(V),
+      seq_lens, sel_idx, sel_cnt, softmax_scale * kLog2e, static_cast<E*>(out), lse, part_o,
+      reinterpret_cast<float2*>(part_ml), p->d_counters, p->d_error, p->desc.num_kv_heads,
+      p->desc.t_cap, p->max_sel, p->split, p->log2split, p->max_chunks);
+  return hipGetLastError();
+}
+
+template <typename E, int D>
+hipError_t dispatch_g(const fx_plan* p, const void* q, const void* K, const void* V,
+                      const int32_t* seq_lens, const int32_t* sel_idx, const int32_t* sel_cnt,
+                      float scale, void* out, float* lse, float* po, float* pml,
+                      hipStream_t s) {
+  switch (p->G) {
+    case 1: return launch_t<E, D, 1>(p, q, K, V, seq_lens, sel_idx, sel_cnt, scale, out, lse, po, pml, s);
+    case 2: return launch_t<E, D, 2>(p, q, K, V, seq_lens, sel_idx, sel_cnt, scale, out, lse, po, pml, s);
+    case 3: return launch_t<E, D, 3>(p, q, K, V, seq_lens, sel_idx, sel_cnt, scale, out, lse, po, pml, s);
+    case 4: return launch_t<E, D, 4>(p, q, K, V, seq_lens, sel_idx, sel_cnt, scale, out, lse, po, pml, s);
+    case 5: return launch_t<E, D, 5>(p, q, K, V, seq_lens, sel_idx, sel_cnt, scale, out, lse, po, pml, s);
+    case 6: return launch_t<E, D, 6>(p, q, K, V, seq_lens, sel_idx, sel_cnt, scale, out, lse, po, pml, s);
+    case 7: return launch_t<E, D, 7>(p, q, K, V, seq_lens, sel_idx, sel_cnt, scale, out, lse, po, pml, s);
+    case 8: return launch_t<E, D, 8>(p, q, K, V, seq_lens, sel_idx, sel_cnt, scale, out, lse, po, pml, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_decode(const fx_plan* p, const void* q, const void* K, const void* V,
+                         const int32_t* seq_lens, const int32_t* sel_idx, const int32_t* sel_cnt,
+                         float softmax_scale, void* out, float* lse, float* part_o,
+                         float* part_ml, hipStream_t stream) {
+  const int d = p->desc.head_dim;
+  if (p->desc.dtype == FX_BF16)
+    return d == 128 ? dispatch_g<bf16_t, 128>(p, q, K, V, seq_lens, sel_idx, sel_cnt,
+                                              softmax_scale, out, lse, part_o, part_ml, stream)
+                    : dispatch_g<bf16_t, 64>(p, q, K, V, seq_lens, sel_idx, sel_cnt,
+                                             softmax_scale, out, lse, part_o, part_ml, stream);
+  return d == 128 ? dispatch_g<float, 128>(p, q, K, V, seq_lens, sel_idx, sel_cnt, softmax_scale,
+                                           out, lse, part_o, part_ml, stream)
+                  : dispatch_g<float, 64>(p, q, K, V, seq_lens, sel_idx, sel_cnt, softmax_scale,
+                                          out, lse, part_o, part_ml, stream);
+}
+
+}  // namespace fx

@@ -1,0 +1,288 @@
+"""HIP library vs CPU oracle, element by element (needs an MI355X).
+
+Bar: summaries, scores, selected indices, eviction masks and deltas bit-exact;
+out within |d| <= atol + rtol |ref| (bf16: rtol 2e-2, atol 1e-2; fp32: 1e-4, 1e-4)
+against the oracle's float64 value; lse within rtol 1e-5, atol 1e-4.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_decode_summary_amd as fx
+from oracle.delta import locality, selection_delta
+from oracle.step import unit_step
+from workloads import (HeadPolicy, MODE_NOSA, MODE_RETRIEVAL, MODE_STREAMING, WORKLOAD_NAMES,
+                       Workload, generate, get_workload, query_at_step, small_workload, unit_arrays)
+
+from gpu_harness import (INT32_MAX, GpuView, compare_unit, make_plan, oracle_unit,
+                         run_select_decode, say, softmax_scale, assert_close, TOL)
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _run_and_compare_all(w: Workload, split_tokens: int = 0, steps: int = 1):
+    say(f"[parity] {w.name}: B={w.batch} Hq={w.num_q_heads} Hkv={w.num_kv_heads} d={w.head_dim} "
+        f"{w.dtype} t_cap={w.t_cap} split={split_tokens} steps={steps}")
+    inp = generate(w, DEV)
+    plan = make_plan(w, split_tokens)
+    bufs = fx.allocate_step_buffers(plan, DEV)
+    evicted = {u: None for u in range(w.num_units)}
+    prev = {u: np.zeros(0, np.int64) for u in range(w.num_units)}
+    for t in range(steps):
+        q = query_at_step(w, t, DEV) if t > 0 else inp.q
+        bufs.prev_idx.copy_(bufs.sel_idx)
+        bufs.prev_cnt.copy_(bufs.sel_cnt)
+        run_select_decode(plan, bufs, inp, q, build=(t == 0))
+        fx.fx_selection_delta(plan, bufs.prev_idx, bufs.prev_cnt, bufs.sel_idx, bufs.sel_cnt,
+                              bufs.added, bufs.added_cnt, bufs.removed, bufs.removed_cnt)
+        gv = GpuView(plan, bufs, w)
+        added = bufs.added.cpu().numpy()
+        added_cnt = bufs.added_cnt.cpu().numpy()
+        removed = bufs.removed.cpu().numpy()
+        removed_cnt = bufs.removed_cnt.cpu().numpy()
+        for u in range(w.num_units):
+            ref = oracle_unit(inp, u, q, evicted[u])
+            compare_unit(w, u, gv, ref)
+            if w.policies[u].mode == MODE_NOSA:
+                n_full = w.seq_lens[u // w.num_kv_heads] // w.policies[u].block
+                got_ev = gv.evicted(u)
+                assert np.array_equal(got_ev[:n_full], ref.evicted[:n_full]), f"unit {u} mask step {t}"
+                assert not got_ev[n_full:].any()
+                evicted[u] = ref.evicted
+                if t > 0:
+                    p = w.policies[u]
+                    assert locality(prev[u], ref.sel) >= p.k_evict / (p.k_evict + p.top_k)
+            a_ref, r_ref = selection_delta(prev[u], ref.sel)
+            assert list(added[u, :added_cnt[u]]) == list(a_ref), f"unit {u} added, step {t}"
+            assert list(removed[u, :removed_cnt[u]]) == list(r_ref), f"unit {u} removed, step {t}"
+            assert np.all(added[u, added_cnt[u]:] == -1) and np.all(removed[u, removed_cnt[u]:] == -1)
+            prev[u] = ref.sel
+    assert fx.fx_read_error(plan) == 0
+    say(f"[parity] {w.name}: ok")
+
+
+@pytest.mark.parametrize("name", WORKLOAD_NAMES)
+def test_parity_small_workloads(name):
+    w = small_workload(name)
+    _run_and_compare_all(w, steps=w.steps)
+
+
+@pytest.mark.parametrize("name", WORKLOAD_NAMES)
+def test_parity_full_size_sampled(name):
+    """Full workload sizes in the launch configuration the benchmark uses; sampled units."""
+    w = get_workload(name)
+    say(f"[full] {name}: generating B={w.batch} t_cap={w.t_cap}")
+    inp = generate(w, DEV)
+    plan = make_plan(w)
+    bufs = fx.allocate_step_buffers(plan, DEV)
+    steps = 2 if w.has_nosa else 1
+    rng = np.random.default_rng(100 + WORKLOAD_NAMES.index(name))
+    units = sorted(set([0, w.num_units - 1] + list(rng.choice(w.num_units, size=min(6, w.num_units),
+                                                              replace=False))))
+    evicted = {u: None for u in units}
+    for t in range(steps):
+        q = query_at_step(w, t, DEV) if t > 0 else inp.q
+        say(f"[full] {name}: step {t} (split {plan.split_tokens}), units {units}")
+        run_select_decode(plan, bufs, inp, q, build=(t == 0))
+        gv = GpuView(plan, bufs, w)
+        for u in units:
+            ref = oracle_unit(inp, u, q, evicted[u])
+            compare_unit(w, u, gv, ref)
+            if w.policies[u].mode == MODE_NOSA:
+                evicted[u] = ref.evicted
+    # Properties at every unit: counts within the plan bound, ascending selections,
+    # finite outputs.
+    cnt = gv.sel_cnt
+    assert np.all(cnt >= 0) and np.all(cnt <= plan.max_selected)
+    for u in range(w.num_units):
+        s = gv.sel_idx[u, :cnt[u]]
+        assert np.all(np.diff(s) > 0)
+    assert np.all(np.isfinite(gv.out))
+    assert fx.fx_read_error(plan) == 0
+    del inp, bufs
+    torch.cuda.empty_cache()
+
+
+def _custom(name, batch, Hq, Hkv, d, dtype, t_cap, lens, pols, seed=50):
+    return Workload(name=name, batch=batch, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=d,
+                    dtype=dtype, t_cap=t_cap, seq_lens=tuple(lens), policies=tuple(pols), seed=seed,
+                    sink_scaled_tokens=4, needles_per_head=2)
+
+
+def test_dense_when_everything_is_selected():
+    """Block size 1 with k = n, and a budget covering all blocks, are dense attention."""
+    T = 300
+    for g, k in ((1, T), (16, 1000)):
+        pol = HeadPolicy(MODE_RETRIEVAL, block=g, sub_block=1, top_k=k)
+        w = _custom(f"dense_g{g}", 1, 4, 2, 64, "bf16", T, [T], [pol, pol])
+        _run_and_compare_all(w)
+        inp = generate(w, DEV)
+        plan = make_plan(w)
+        bufs = fx.allocate_step_buffers(plan, DEV)
+        run_select_decode(plan, bufs, inp, inp.q)
+        torch.cuda.synchronize()
+        qf = inp.q.double().cpu()
+        Kf = inp.K.double().cpu()
+        Vf = inp.V.double().cpu()
+        for h in range(2):
+            qr = qf[0, 2 * h:2 * h + 2]
+            s = (qr @ Kf[0, h, :T].T) / math.sqrt(64)
+            dense = torch.softmax(s, dim=-1) @ Vf[0, h, :T]
+            assert_close("dense", bufs.out[0, 2 * h:2 * h + 2].double().cpu().numpy(), dense.numpy(),
+                         *TOL["bf16"])
+
+
+def test_ragged_degenerate_lengths_and_mixed_modes():
+    lens = [0, 1, 15, 16, 17, 1000]
+    pols = []
+    for _ in lens:
+        pols += [HeadPolicy(MODE_RETRIEVAL, block=16, sub_block=4, top_k=3, force_sink=1, force_last=1),
+                 HeadPolicy(MODE_STREAMING, block=16, sub_block=16, sink_tokens=5, local_tokens=20),
+                 HeadPolicy(MODE_NOSA, block=16, sub_block=8, top_k=2, k_evict=2)]
+    w = _custom("ragged_mixed", len(lens), 6, 3, 128, "bf16", 1024, lens, pols)
+    _run_and_compare_all(w, steps=1)
+    for split in (64, 2048):
+        _run_and_compare_all(w.replace(name=f"ragged_mixed_s{split}"), split_tokens=split)
+
+
+@pytest.mark.parametrize("G,d,dtype", [(1, 128, "bf16"), (3, 128, "bf16"), (8, 128, "bf16"),
+                                       (2, 64, "bf16"), (5, 128, "f32"), (8, 64, "f32")])
+def test_group_sizes_and_head_dims(G, d, dtype):
+    Hkv = 2
+    pol = HeadPolicy(MODE_RETRIEVAL, block=32, sub_block=16, budget=float(np.float32(0.1)),
+                     force_sink=1, force_last=1)
+    w = _custom(f"g{G}_d{d}_{dtype}", 2, G * Hkv, Hkv, d, dtype, 3000, [3000, 2211],
+                [pol] * (2 * Hkv))
+    _run_and_compare_all(w)
+
+
+def test_split_invariance_and_determinism():
+    w = small_workload("qwen7b_layer")
+    inp = generate(w, DEV)
+    outs = []
+    sels = []
+    for split in (64, 256, 2048):
+        plan = make_plan(w, split)
+        bufs = fx.allocate_step_buffers(plan, DEV)
+        run_select_decode(plan, bufs, inp, inp.q)
+        o1 = bufs.out.clone()
+        run_select_decode(plan, bufs, inp, inp.q)
+        assert torch.equal(o1, bufs.out), f"split {split}: two runs differ"
+        outs.append(o1.double().cpu().numpy())
+        sels.append(bufs.sel_idx.cpu().numpy().copy())
+    for s in sels[1:]:
+        assert np.array_equal(s, sels[0])
+    for o in outs[1:]:
+        assert_close("split", o, outs[0], 2e-2, 1e-2)
+
+
+def test_score_ties_prefer_lower_index():
+    g, T = 16, 16 * 40
+    pol = HeadPolicy(MODE_RETRIEVAL, block=g, sub_block=16, top_k=3, force_sink=0, force_last=0)
+    w = _custom("ties", 1, 2, 1, 128, "bf16", T, [T], [pol])
+    inp = generate(w, DEV)
+    # Five identical copies of needle block 7 (high scores) at blocks 7, 9, 20, 30, 33.
+    src = inp.K[0, 0, 7 * g:8 * g].clone()
+    src += 3.0 * inp.q[0, 0:2].float().mean(0).to(src.dtype)
+    for j in (7, 9, 20, 30, 33):
+        inp.K[0, 0, j * g:(j + 1) * g] = src
+    plan = make_plan(w)
+    bufs = fx.allocate_step_buffers(plan, DEV)
+    run_select_decode(plan, bufs, inp, inp.q)
+    gv = GpuView(plan, bufs, w)
+    ref = oracle_unit(inp, 0, inp.q)
+    compare_unit(w, 0, gv, ref)
+    assert list(gv.unit(0).sel) == [7, 9, 20]
+
+
+def test_summary_is_rounded_once():
+    """A sub-block mean just above a bfloat16 tie: one rounding gives 241/256, two give 240/256."""
+    g = 16
+    pol = HeadPolicy(MODE_RETRIEVAL, block=g, sub_block=16, top_k=1)
+    w = _custom("single_rounding", 1, 1, 1, 64, "bf16", 2 * g, [2 * g], [pol])
+    inp = generate(w, DEV)
+    col = torch.zeros(g, dtype=torch.float64)
+    col[:14] = 1.0
+    col[14] = 1.0 + 2.0 ** -5
+    col[15] = 2.0 ** -36
+    inp.K[0, 0, :g, 5] = col.to(torch.bfloat16).to(DEV)
+    plan = make_plan(w)
+    bufs = fx.allocate_step_buffers(plan, DEV)
+    fx.fx_build_summaries(plan, inp.K, inp.seq_lens, 0, INT32_MAX, bufs.summaries)
+    torch.cuda.synchronize()
+    assert bufs.summaries[5].item() == 241 * 2.0 ** -8
+    ref = oracle_unit(inp, 0, inp.q)
+    got = bufs.summaries.double().cpu().numpy().reshape(-1, 64)[:2]
+    assert np.array_equal(got, ref.summaries)
+
+
+def test_incremental_summary_build():
+    w = small_workload("llama8b_layer")
+    inp = generate(w, DEV)
+    plan = make_plan(w)
+    bufs = fx.allocate_step_buffers(plan, DEV)
+    fx.fx_build_summaries(plan, inp.K, inp.seq_lens, 0, INT32_MAX, bufs.summaries)
+    g = 64
+    n_full = w.seq_lens[0] // g
+    inp.K[0, :, (n_full - 1) * g:n_full * g] *= -2       # change the newest full block
+    before = bufs.summaries.clone()
+    fx.fx_build_summaries(plan, inp.K, inp.seq_lens, -1, INT32_MAX, bufs.summaries)
+    incr = bufs.summaries.clone()
+    fx.fx_build_summaries(plan, inp.K, inp.seq_lens, 0, INT32_MAX, bufs.summaries)
+    assert torch.equal(incr, bufs.summaries)
+    changed = (incr.view(-1, 128) != before.view(-1, 128)).any(dim=1).nonzero().flatten().cpu()
+    offs = w.block_offsets()
+    assert set(changed.tolist()) <= {int(offs[u]) + n_full - 1 for u in range(w.num_units)}
+    assert len(changed) > 0
+
+
+def test_selection_delta_random_lists():
+    pol = HeadPolicy(MODE_RETRIEVAL, block=16, sub_block=16, top_k=200)
+    w = _custom("delta", 4, 4, 2, 64, "bf16", 16 * 400, [6400] * 4, [pol] * 8)
+    plan = make_plan(w)
+    ms = plan.max_selected
+    rng = np.random.default_rng(7)
+    prev = np.full((8, ms), -1, np.int32)
+    cur = np.full((8, ms), -1, np.int32)
+    pc = np.zeros(8, np.int32)
+    cc = np.zeros(8, np.int32)
+    for u in range(8):
+        a = np.sort(rng.choice(400, size=int(rng.integers(0, ms + 1)), replace=False))
+        c = np.sort(rng.choice(400, size=int(rng.integers(0, ms + 1)), replace=False))
+        prev[u, :a.size], pc[u] = a, a.size
+        cur[u, :c.size], cc[u] = c, c.size
+    bufs = fx.allocate_step_buffers(plan, DEV)
+    t = lambda x: torch.from_numpy(x).to(DEV)
+    fx.fx_selection_delta(plan, t(prev), t(pc), t(cur), t(cc), bufs.added, bufs.added_cnt,
+                          bufs.removed, bufs.removed_cnt)
+    torch.cuda.synchronize()
+    for u in range(8):
+        ar, rr = selection_delta(prev[u, :pc[u]], cur[u, :cc[u]])
+        assert list(bufs.added[u, :bufs.added_cnt[u]].cpu()) == list(ar)
+        assert list(bufs.removed[u, :bufs.removed_cnt[u]].cpu()) == list(rr)
+
+
+def test_bad_device_data_is_flagged_not_faulting():
+    """seq_len beyond t_cap and out-of-range selection entries are clamped / skipped by the
+    kernels' own checks and reported in the error word."""
+    w = small_workload("tiny")
+    inp = generate(w, DEV)
+    plan = make_plan(w)
+    bufs = fx.allocate_step_buffers(plan, DEV)
+    bad_lens = torch.tensor([w.t_cap + 100], dtype=torch.int32, device=DEV)
+    fx.fx_build_summaries(plan, inp.K, bad_lens, 0, INT32_MAX, bufs.summaries)
+    fx.fx_select(plan, inp.q, bufs.summaries, None, None, bad_lens, bufs.sel_idx, bufs.sel_cnt,
+                 bufs.workspace)
+    torch.cuda.synchronize()
+    assert fx.fx_read_error(plan) & fx.FX_ERR_SEQ_LEN
+    sel = bufs.sel_idx.clone()
+    sel[0, 1] = 10_000                                      # outside the unit's blocks
+    sel[1, 2] = sel[1, 1]                                   # not ascending
+    fx.fx_sparse_decode(plan, inp.q, inp.K, inp.V, inp.seq_lens, sel, bufs.sel_cnt,
+                        softmax_scale(w), bufs.out, bufs.lse, bufs.workspace)
+    torch.cuda.synchronize()
+    assert fx.fx_read_error(plan) & fx.FX_ERR_SEL_INDEX
+    assert torch.isfinite(bufs.out).all()
