@@ -63,12 +63,12 @@ _P = ctypes.c_void_p
 _I32 = ctypes.c_int32
 
 
-def load_library():
-    """Load libfx.so (once).  Raises if it has not been built."""
+def load_library(path: Optional[str] = None):
+    """Load libfx.so (once; `path` overrides the in-tree build).  Raises if it is missing."""
     global _lib
-    if _lib is not None:
+    if _lib is not None and path is None:
         return _lib
-    path = library_path()
+    path = path or library_path()
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run `python -m block_sparse_decode_summary_amd.build`")
     lib = ctypes.CDLL(path)

@@ -163,10 +163,9 @@ fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_pl
   off += align_up((size_t)units * p->max_chunks * p->G * 8, 256);
   p->ws_total = std::max<size_t>(off, 256);
 
-  // Device table: units | counters | error word.
+  // Device table: units | error word.
   const size_t tab_units = align_up(sizeof(UnitInfo) * units, 256);
-  const size_t tab_cnt = align_up(sizeof(int32_t) * units, 256);
-  const size_t tab_bytes = tab_units + tab_cnt + 256;
+  const size_t tab_bytes = tab_units + 256;
   if (hipGetDevice(&p->device) != hipSuccess ||
       hipMalloc(&p->d_table, tab_bytes) != hipSuccess) {
     delete p;
@@ -174,11 +173,10 @@ fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_pl
   }
   char* base = static_cast<char*>(p->d_table);
   p->d_units = reinterpret_cast<UnitInfo*>(base);
-  p->d_counters = reinterpret_cast<int32_t*>(base + tab_units);
-  p->d_error = reinterpret_cast<uint32_t*>(base + tab_units + tab_cnt);
+  p->d_error = reinterpret_cast<uint32_t*>(base + tab_units);
   if (hipMemcpy(p->d_units, p->host_units.data(), sizeof(UnitInfo) * units,
                 hipMemcpyHostToDevice) != hipSuccess ||
-      hipMemset(base + tab_units, 0, tab_cnt + 256) != hipSuccess) {
+      hipMemset(base + tab_units, 0, 256) != hipSuccess) {
     (void)hipFree(p->d_table);
     delete p;
     return FX_E_HIP;

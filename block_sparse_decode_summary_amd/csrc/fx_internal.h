@@ -46,10 +46,9 @@ struct fx_plan {
   int32_t units = 0;
   std::vector<fx::UnitInfo> host_units;
   int device = 0;
-  // device table: [units] UnitInfo | [units] int32 split-K counters | uint32 error word
+  // device table: [units] UnitInfo | uint32 error word
   void* d_table = nullptr;
   fx::UnitInfo* d_units = nullptr;
-  int32_t* d_counters = nullptr;
   uint32_t* d_error = nullptr;
 
   int64_t total_blocks = 0;

@@ -1,4 +1,4 @@
-// Split-K flash-decoding over the selected blocks, with the chunk merge fused in.
+// Split-K flash-decoding over the selected blocks, then a chunk merge.
 //
 // [Fluxion-NL] "Technische Samenvatting: Fluxion", Probleemstelling item 1: after
 // top-k block selection, attention runs over the selected KV blocks only; Kerninzichten
@@ -14,17 +14,21 @@
 // lives in selected block i / g at offset i % g.  Chunks of `split` tokens are one
 // workgroup each (grid = units x max_chunks; chunks past the unit's N exit at once).
 //
-// Inside a workgroup (4 waves), a token's d-vector is spread over LPT lanes, each lane
-// holding 16 bytes (8 bfloat16 / 4 float32) of the K and V rows: every load is a
-// 128-bit load and each wave instruction reads 64 x 16 contiguous bytes per 64/LPT
-// tokens.  Each lane keeps the G query rows' matching 16 bytes in registers, forms G
-// partial dot products (v_dot2_f32_bf16 for bfloat16), and DPP-reduces them across its
-// LPT lanes.  The online softmax runs in base 2 (scores pre-multiplied by
-// scale*log2(e)) per lane group; U tokens per lane group per step amortise the rescale.
-// Lane groups, then waves, merge with the log-sum-exp rule; a unit with one chunk
-// writes `out` directly.  Otherwise each chunk writes (o, m, l) to the workspace and
-// bumps the unit's counter; the last chunk to arrive merges all chunks in chunk order
-// (so the result does not depend on scheduling) and resets the counter.
+// k_decode (4 waves per chunk): a token's d-vector is spread over LPT lanes, each lane
+// holding 16 bytes (8 bfloat16 / 4 float32) of the K and V rows, so every load is a
+// 128-bit load and each wave instruction reads 64/LPT whole rows.  Loads for the next
+// step of U tokens per lane group are issued before the current step is computed
+// (register double buffering), so two steps of K and V are in flight per wave.  Each
+// lane keeps the G query rows' matching 16 bytes in registers, forms G partial dot
+// products (v_dot2_f32_bf16 for bfloat16) and DPP-reduces them across its LPT lanes.
+// The online softmax runs in base 2 (scores pre-multiplied by scale*log2(e)) per lane
+// group.  Lane groups, then waves, merge with the log-sum-exp rule.  A unit with one
+// chunk writes `out` directly; otherwise each chunk writes its unnormalised (o, m, l).
+//
+// k_combine (one workgroup per unit with more than one chunk) merges the chunk
+// partials in chunk order, so results do not depend on scheduling.  The kernel
+// boundary makes every chunk's partial visible to it; no fence is needed inside
+// k_decode (an agent-scope fence per workgroup would write back the L2 each time).
 #include "fx_device.h"
 
 namespace fx {
@@ -81,14 +85,44 @@ __device__ __forceinline__ void unpack(const uint4& v, float* f, float*) {
   f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
 }
 
+// Selected-token count of a unit and its chunk count (identical in both kernels).
+struct UnitSpan {
+  int T, cnt, N, nchunks;
+};
+
+__device__ __forceinline__ UnitSpan unit_span(const UnitInfo& ui, const int32_t* seq_lens,
+                                              const int32_t* sel, const int32_t* sel_cnt, int u,
+                                              int b, int t_cap, int max_sel, int split,
+                                              int log2split, int max_chunks, uint32_t* err) {
+  UnitSpan s;
+  s.T = load_seq_len(seq_lens, b, t_cap, err);
+  int cnt = sel_cnt[u];
+  if (cnt < 0 || cnt > max_sel) {
+    if (threadIdx.x == 0) atomicOr(err, (uint32_t)FX_ERR_SEL_COUNT);
+    cnt = cnt < 0 ? 0 : max_sel;
+  }
+  s.cnt = cnt;
+  int N = 0;
+  if (cnt > 0) {
+    const int last = sel[cnt - 1];
+    const int valid_last = min(max(s.T - last * ui.g, 0), ui.g);
+    N = (cnt - 1) * ui.g + valid_last;
+  }
+  if (N > max_chunks * split) {   // only for selections that are not valid for this unit
+    if (threadIdx.x == 0) atomicOr(err, (uint32_t)FX_ERR_SEL_INDEX);
+    N = max_chunks * split;
+  }
+  s.N = N;
+  s.nchunks = N > 0 ? ((N + split - 1) >> log2split) : 1;
+  return s;
+}
+
 template <typename E, int D, int G>
 struct DecodeLds {
-  static constexpr int EPL = Lanes<E>::EPL;
   int blk[kMaxSplit + 1];          // selected block indices covering this chunk
   float o[NWAVES][G][D];
   float m[NWAVES][G];
   float l[NWAVES][G];
-  int last;
 };
 
 template <typename E, int D, int G, int U>
@@ -97,11 +131,12 @@ __global__ __launch_bounds__(NT) void k_decode(
     const E* __restrict__ V, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ sel_cnt, float scale_log2,
     E* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
-    float2* __restrict__ part_ml, int32_t* __restrict__ counters, uint32_t* __restrict__ err,
-    int Hkv, int t_cap, int max_sel, int split, int log2split, int max_chunks) {
+    float2* __restrict__ part_ml, uint32_t* __restrict__ err, int Hkv, int t_cap, int max_sel,
+    int split, int log2split, int max_chunks) {
   constexpr int EPL = Lanes<E>::EPL;
   constexpr int LPT = D / EPL;        // lanes per token
   constexpr int TPW = 64 / LPT;       // tokens per wave instruction
+  constexpr int STEP = TPW * U;       // tokens per wave per step
   static_assert(LPT >= 4 && LPT <= 32 && 64 % LPT == 0, "lane layout");
   __shared__ DecodeLds<E, D, G> L;
 
@@ -109,31 +144,16 @@ __global__ __launch_bounds__(NT) void k_decode(
   const int chunk = blockIdx.x % max_chunks;
   const UnitInfo ui = units[u];
   const int b = u / Hkv, h = u % Hkv;
-  const int T = load_seq_len(seq_lens, b, t_cap, err);
-  const int g = ui.g, log2g = ui.log2g;
-
-  int cnt = sel_cnt[u];
-  if (cnt < 0 || cnt > max_sel) {
-    if (threadIdx.x == 0) atomicOr(err, (uint32_t)FX_ERR_SEL_COUNT);
-    cnt = cnt < 0 ? 0 : max_sel;
-  }
   const int32_t* sel = sel_idx + (size_t)u * max_sel;
-  int N = 0;
-  if (cnt > 0) {
-    const int last = sel[cnt - 1];
-    const int valid_last = min(max(T - last * g, 0), g);
-    N = (cnt - 1) * g + valid_last;
-  }
-  if (N > max_chunks * split) {   // only for selections that are not valid for this unit
-    if (threadIdx.x == 0) atomicOr(err, (uint32_t)FX_ERR_SEL_INDEX);
-    N = max_chunks * split;
-  }
-  const int nchunks = N > 0 ? ((N + split - 1) >> log2split) : 1;
-  if (chunk >= nchunks) return;
+  const UnitSpan sp = unit_span(ui, seq_lens, sel, sel_cnt, u, b, t_cap, max_sel, split,
+                                log2split, max_chunks, err);
+  if (chunk >= sp.nchunks) return;
+  const int T = sp.T, g = ui.g, log2g = ui.log2g;
 
   const int i0 = chunk << log2split;
-  const int i1 = min(N, i0 + split);
-  // Block indices this chunk touches.
+  const int i1 = min(sp.N, i0 + split);
+  // Block indices this chunk touches; entries that are not valid blocks of the unit, in
+  // ascending order, become -1 (their tokens are skipped).
   const int p0 = i0 >> log2g;
   const int np = i1 > i0 ? ((i1 - 1) >> log2g) - p0 + 1 : 0;
   for (int i = threadIdx.x; i < np; i += NT) {
@@ -170,9 +190,7 @@ __global__ __launch_bounds__(NT) void k_decode(
   const E* Kb = K + unit_rows * D + li * EPL;
   const E* Vb = V + unit_rows * D + li * EPL;
 
-  for (int base = w0; base < w1; base += TPW * U) {
-    uint4 kr[U], vr[U];
-    bool ok[U];
+  auto load_step = [&](int base, uint4* kr, uint4* vr, bool* ok) {
 #pragma unroll
     for (int uu = 0; uu < U; ++uu) {
       const int i = base + uu * TPW + lg;
@@ -190,6 +208,9 @@ __global__ __launch_bounds__(NT) void k_decode(
         vr[uu] = make_uint4(0, 0, 0, 0);
       }
     }
+  };
+
+  auto compute_step = [&](const uint4* kr, const uint4* vr, const bool* ok) {
     float s[U][G];
 #pragma unroll
     for (int uu = 0; uu < U; ++uu)
@@ -224,6 +245,21 @@ __global__ __launch_bounds__(NT) void k_decode(
       }
       l[gg] = lsum;
     }
+  };
+
+  // Register double buffering: the loads of step n+1 are in flight while step n computes.
+  uint4 kA[U], vA[U], kB[U], vB[U];
+  bool okA[U], okB[U];
+  int base = w0;
+  if (base < w1) load_step(base, kA, vA, okA);
+  while (base < w1) {
+    if (base + STEP < w1) load_step(base + STEP, kB, vB, okB);
+    compute_step(kA, vA, okA);
+    base += STEP;
+    if (base >= w1) break;
+    if (base + STEP < w1) load_step(base + STEP, kA, vA, okA);
+    compute_step(kB, vB, okB);
+    base += STEP;
   }
 
   // Merge the lane groups of the wave (partners differ in the lane bits above LPT).
@@ -259,7 +295,7 @@ __global__ __launch_bounds__(NT) void k_decode(
   __syncthreads();
 
   // Merge the waves in wave order; then either finish the unit or publish a partial.
-  const bool single = nchunks == 1;
+  const bool single = sp.nchunks == 1;
   const size_t pbase = (size_t)u * max_chunks + chunk;
   for (int idx = threadIdx.x; idx < G * D; idx += NT) {
     const int gg = idx / D, c = idx % D;
@@ -282,26 +318,28 @@ __global__ __launch_bounds__(NT) void k_decode(
       if (c == 0) part_ml[pbase * G + gg] = make_float2(M, Ls);
     }
   }
-  if (single) return;
+}
 
-  // Last-arriver merge.  Release: make this chunk's partial visible device-wide
-  // (agent-scope fence writes back this XCD's L2) before counting it.
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const int prev = atomicAdd(&counters[u], 1);
-    L.last = prev == nchunks - 1;
-  }
-  __syncthreads();
-  if (!L.last) return;
-  __threadfence();   // acquire: see every other chunk's partial
+template <typename E, int D, int G>
+__global__ __launch_bounds__(NT) void k_combine(
+    const UnitInfo* __restrict__ units, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ sel_cnt,
+    E* __restrict__ out, float* __restrict__ lse, const float* __restrict__ part_o,
+    const float2* __restrict__ part_ml, uint32_t* __restrict__ err, int Hkv, int t_cap,
+    int max_sel, int split, int log2split, int max_chunks) {
+  const int u = blockIdx.x;
+  const UnitInfo ui = units[u];
+  const int b = u / Hkv, h = u % Hkv;
+  const UnitSpan sp = unit_span(ui, seq_lens, sel_idx + (size_t)u * max_sel, sel_cnt, u, b,
+                                t_cap, max_sel, split, log2split, max_chunks, err);
+  if (sp.nchunks == 1) return;   // k_decode already wrote this unit
   const size_t ubase = (size_t)u * max_chunks;
   for (int idx = threadIdx.x; idx < G * D; idx += NT) {
     const int gg = idx / D, c = idx % D;
     float M = kNegBig;
-    for (int k = 0; k < nchunks; ++k) M = fmaxf(M, part_ml[(ubase + k) * G + gg].x);
+    for (int k = 0; k < sp.nchunks; ++k) M = fmaxf(M, part_ml[(ubase + k) * G + gg].x);
     float Ls = 0.0f, Os = 0.0f;
-    for (int k = 0; k < nchunks; ++k) {
+    for (int k = 0; k < sp.nchunks; ++k) {
       const float2 ml = part_ml[(ubase + k) * G + gg];
       const float a = __builtin_amdgcn_exp2f(ml.x - M);
       Ls = fmaf(ml.y, a, Ls);
@@ -311,7 +349,6 @@ __global__ __launch_bounds__(NT) void k_decode(
     store_elem(out + orow * D + c, Ls > 0.0f ? Os / Ls : 0.0f);
     if (lse && c == 0) lse[orow] = Ls > 0.0f ? (M + __log2f(Ls)) * kLn2 : -__builtin_inff();
   }
-  if (threadIdx.x == 0) counters[u] = 0;
 }
 
 template <typename E, int D, int G>
@@ -320,12 +357,19 @@ hipError_t launch_t(const fx_plan* p, const void* q, const void* K, const void* 
                     float softmax_scale, void* out, float* lse, float* part_o, float* part_ml,
                     hipStream_t stream) {
   constexpr int U = 4;
+  const int Hkv = p->desc.num_kv_heads, t_cap = p->desc.t_cap;
   const dim3 grid((unsigned)((int64_t)p->units * p->max_chunks));
   k_decode<E, D, G, U><<<grid, NT, 0, stream>>>(
       p->d_units, static_cast<const E*>(q), static_cast<const E*>(K), static_cast<const E*>(V),
       seq_lens, sel_idx, sel_cnt, softmax_scale * kLog2e, static_cast<E*>(out), lse, part_o,
-      reinterpret_cast<float2*>(part_ml), p->d_counters, p->d_error, p->desc.num_kv_heads,
-      p->desc.t_cap, p->max_sel, p->split, p->log2split, p->max_chunks);
+      reinterpret_cast<float2*>(part_ml), p->d_error, Hkv, t_cap, p->max_sel, p->split,
+      p->log2split, p->max_chunks);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p->max_chunks == 1) return e;
+  k_combine<E, D, G><<<dim3((unsigned)p->units), NT, 0, stream>>>(
+      p->d_units, seq_lens, sel_idx, sel_cnt, static_cast<E*>(out), lse, part_o,
+      reinterpret_cast<const float2*>(part_ml), p->d_error, Hkv, t_cap, p->max_sel, p->split,
+      p->log2split, p->max_chunks);
   return hipGetLastError();
 }
 

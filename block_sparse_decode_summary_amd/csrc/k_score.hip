@@ -17,7 +17,8 @@
 // Mapping: one wave per tile of 64 blocks of one unit.  qs goes to LDS once per
 // workgroup; the tile's summary rows are staged into LDS with 16-byte loads (row
 // stride WORDS+1 words, so lane i reading word c of row i hits bank (i + c) mod 64);
-// then lane i runs block j0 + i's d-term chain in order.
+// then lane i runs block j0 + i's d-term chain in order.  Each lane issues all of its
+// staging loads before writing any of them, so a tile costs one memory round trip.
 #include "fx_device.h"
 
 namespace fx {
@@ -60,15 +61,28 @@ __global__ __launch_bounds__(64) void k_score(
     for (int g = 1; g < G; ++g) a = a + (double)to_f32(qg[(size_t)g * D + c]);
     qs[c] = a;
   }
+  // Stage the tile: every lane issues all of its 16-byte loads before the first LDS
+  // write, so the tile costs one memory round trip.
   const uint4* src = reinterpret_cast<const uint4*>(S + ((size_t)ui.block_off + j0) * D);
-  constexpr int V4 = WORDS / 4;   // 16-byte vectors per row
-  for (int i = lane; i < nrows * V4; i += 64) {
-    const uint4 v = src[i];
-    const int r = i / V4, c = (i % V4) * 4;
-    rows[r][c + 0] = v.x;
-    rows[r][c + 1] = v.y;
-    rows[r][c + 2] = v.z;
-    rows[r][c + 3] = v.w;
+  constexpr int V4 = WORDS / 4;                 // 16-byte vectors per row
+  constexpr int PER_LANE = kTile * V4 / 64;
+  const int nvec = nrows * V4;
+  uint4 buf[PER_LANE];
+#pragma unroll
+  for (int k = 0; k < PER_LANE; ++k) {
+    const int i = lane + k * 64;
+    buf[k] = i < nvec ? src[i] : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int k = 0; k < PER_LANE; ++k) {
+    const int i = lane + k * 64;
+    if (i < nvec) {
+      const int r = i / V4, c = (i % V4) * 4;
+      rows[r][c + 0] = buf[k].x;
+      rows[r][c + 1] = buf[k].y;
+      rows[r][c + 2] = buf[k].z;
+      rows[r][c + 3] = buf[k].w;
+    }
   }
   __syncthreads();
   if (lane >= nrows) return;

@@ -52,12 +52,12 @@
  *
  * Ownership and ordering
  *   The caller owns every buffer, stream and the eviction mask.  A plan owns only
- *   a small device table (per-unit policies, split-K counters, an error word),
- *   allocated by fx_plan_create and freed by fx_plan_destroy.  The four hot
- *   calls never allocate, never synchronise and never copy between host and
- *   device: they enqueue kernels on `stream` and return.  A plan must be used
- *   from one stream at a time (calls on one plan that overlap in time race on
- *   its counters).
+ *   a small device table (per-unit policies and an error word), allocated by
+ *   fx_plan_create and freed by fx_plan_destroy; the hot calls only read it (and
+ *   set error bits).  The four hot calls never allocate, never synchronise and
+ *   never copy between host and device: they enqueue kernels on `stream` and
+ *   return.  Calls that overlap in time must not share a workspace or output
+ *   buffers.
  *
  * Errors
  *   Every call validates its host-side arguments first; on failure it returns a
@@ -223,8 +223,8 @@ fx_status fx_select(fx_plan_t plan, const void* q, const void* summaries,
  * selected blocks, s_t = softmax_scale * (q . K_t); out = sum_t e^{s_t - m} V_t / l
  * with m = max s_t and l = sum_t e^{s_t - m}; lse = m + ln l.  Computed as
  * split-K flash-decoding (float32 online softmax per chunk of selected tokens,
- * then a log-sum-exp merge of the chunks in chunk order, so results do not depend
- * on scheduling).  A unit with no valid token gets out = 0, lse = -inf.
+ * then a log-sum-exp merge of the chunks in chunk order in a second kernel, so
+ * results do not depend on scheduling).  A unit with no valid token gets out = 0, lse = -inf.
  * sel_idx / sel_cnt as written by fx_select (any ascending list of valid block
  * indices of the unit is accepted).  lse may be NULL.  workspace as for fx_select
  * (the two calls may share one workspace; they use disjoint parts of it). */

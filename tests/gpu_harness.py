@@ -116,7 +116,8 @@ def assert_close(name: str, got: np.ndarray, ref: np.ndarray, rtol: float, atol:
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     both_neginf = np.isneginf(got) & np.isneginf(ref)
-    err = np.where(both_neginf, 0.0, np.abs(got - ref))
+    with np.errstate(invalid="ignore"):
+        err = np.where(both_neginf, 0.0, np.abs(got - ref))
     lim = atol + rtol * np.abs(np.where(both_neginf, 0.0, ref))
     bad = ~(err <= lim)
     if np.any(bad):

@@ -184,9 +184,10 @@ def test_score_ties_prefer_lower_index():
     pol = HeadPolicy(MODE_RETRIEVAL, block=g, sub_block=16, top_k=3, force_sink=0, force_last=0)
     w = _custom("ties", 1, 2, 1, 128, "bf16", T, [T], [pol])
     inp = generate(w, DEV)
-    # Five identical copies of needle block 7 (high scores) at blocks 7, 9, 20, 30, 33.
+    # Five identical copies of one block aligned with the query (scores far above the
+    # needles') at blocks 7, 9, 20, 30, 33; top-3 must take the three lowest indices.
     src = inp.K[0, 0, 7 * g:8 * g].clone()
-    src += 3.0 * inp.q[0, 0:2].float().mean(0).to(src.dtype)
+    src += 10.0 * inp.q[0, 0:2].float().mean(0).to(src.dtype)
     for j in (7, 9, 20, 30, 33):
         inp.K[0, 0, j * g:(j + 1) * g] = src
     plan = make_plan(w)
