@@ -42,6 +42,9 @@ fx_status check_desc(const fx_plan_desc* d) {
        d->split_tokens > fx::kMaxSplit))
     return FX_E_INVALID;
   if ((int64_t)d->batch * d->num_kv_heads > (1 << 20)) return FX_E_INVALID;
+  // One unit's K (or V) rows are addressed with 32-bit byte offsets below 2^31.
+  const int64_t unit_bytes = (int64_t)d->t_cap * d->head_dim * (d->dtype == FX_BF16 ? 2 : 4);
+  if (unit_bytes > 0x7FFFFFFF) return FX_E_UNSUPPORTED;
   return FX_OK;
 }
 

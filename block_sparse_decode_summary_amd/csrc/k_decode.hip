@@ -11,19 +11,25 @@
 //   out = sum_t e^{s_t - m} V_t / l,  l = sum_t e^{s_t - m},  lse = m + ln l.
 // The selected tokens of a unit are numbered i = 0 .. N-1 in ascending order; because
 // only the last block of a unit can be partial and selections are ascending, token i
-// lives in selected block i / g at offset i % g.  Chunks of `split` tokens are one
-// workgroup each (grid = units x max_chunks; chunks past the unit's N exit at once).
+// lives in selected block i / g at offset i % g.  A unit's N tokens are cut into
+// nchunks = ceil(N / split) chunks of equal length (rounded up to 16 tokens), one
+// workgroup each (grid = units x max_chunks; chunks past the unit's count exit at once).
 //
 // k_decode (4 waves per chunk): a token's d-vector is spread over LPT lanes, each lane
 // holding 16 bytes (8 bfloat16 / 4 float32) of the K and V rows, so every load is a
-// 128-bit load and each wave instruction reads 64/LPT whole rows.  Loads for the next
-// step of U tokens per lane group are issued before the current step is computed
-// (register double buffering), so two steps of K and V are in flight per wave.  Each
-// lane keeps the G query rows' matching 16 bytes in registers, forms G partial dot
-// products (v_dot2_f32_bf16 for bfloat16) and DPP-reduces them across its LPT lanes.
-// The online softmax runs in base 2 (scores pre-multiplied by scale*log2(e)) per lane
-// group.  Lane groups, then waves, merge with the log-sum-exp rule.  A unit with one
-// chunk writes `out` directly; otherwise each chunk writes its unnormalised (o, m, l).
+// 128-bit load and each wave instruction reads 64/LPT whole rows.  K and V are read
+// through raw buffer resources bounded to the unit's T valid rows: masked token slots
+// get an out-of-range offset and read zeros without a branch or a memory access.
+// Loads for the next step of U tokens per lane group are issued before the current
+// step is computed (register double buffering), so two steps are in flight per wave.
+// Each lane keeps the G query rows' matching 16 bytes in registers, forms G partial
+// dot products (v_dot2_f32_bf16 for bfloat16) and DPP-reduces them across its LPT
+// lanes.  The online softmax runs in base 2 (scores pre-multiplied by scale*log2(e))
+// per lane group, rescaling o and l only in steps where some running max grew.  For
+// bfloat16 the P.V update takes tokens in pairs: p is rounded to bfloat16 and one
+// v_dot2_f32_bf16 per (row, column) accumulates both tokens.  Lane groups, then waves,
+// merge with the log-sum-exp rule.  A unit with one chunk writes `out` directly;
+// otherwise each chunk writes its unnormalised (o, m, l).
 //
 // k_combine (one workgroup per unit with more than one chunk) merges the chunk
 // partials in chunk order, so results do not depend on scheduling.  The kernel
@@ -74,20 +80,49 @@ __device__ __forceinline__ float lane_dot(const uint4& qv, const uint4& kv, floa
   return acc;
 }
 
-__device__ __forceinline__ void unpack(const uint4& v, float* f, bf16_t*) {
-  f[0] = bf16_lo(v.x); f[1] = bf16_hi(v.x);
-  f[2] = bf16_lo(v.y); f[3] = bf16_hi(v.y);
-  f[4] = bf16_lo(v.z); f[5] = bf16_hi(v.z);
-  f[6] = bf16_lo(v.w); f[7] = bf16_hi(v.w);
-}
 __device__ __forceinline__ void unpack(const uint4& v, float* f, float*) {
   f[0] = __uint_as_float(v.x); f[1] = __uint_as_float(v.y);
   f[2] = __uint_as_float(v.z); f[3] = __uint_as_float(v.w);
 }
 
+// o[g][2w], o[g][2w+1] += p_a * v_a + p_b * v_b for one pair of tokens (a, b) of this
+// lane, with p rounded to bfloat16: v_perm_b32 pairs the two tokens' element of each
+// column into one dword and v_dot2_f32_bf16 does both products and the accumulation.
+template <int G>
+__device__ __forceinline__ void pv_pair(const float* pa, const float* pb, const uint4& va,
+                                        const uint4& vb, float (*o)[8]) {
+  bf16x2_t pk[G];
+#pragma unroll
+  for (int gg = 0; gg < G; ++gg) pk[gg] = bf16x2_t{(__bf16)pa[gg], (__bf16)pb[gg]};
+  const uint32_t a[4] = {va.x, va.y, va.z, va.w};
+  const uint32_t b[4] = {vb.x, vb.y, vb.z, vb.w};
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const bf16x2_t lo = __builtin_bit_cast(bf16x2_t, __builtin_amdgcn_perm(b[w], a[w], 0x05040100u));
+    const bf16x2_t hi = __builtin_bit_cast(bf16x2_t, __builtin_amdgcn_perm(b[w], a[w], 0x07060302u));
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg) {
+      o[gg][2 * w] = __builtin_amdgcn_fdot2_f32_bf16(pk[gg], lo, o[gg][2 * w], false);
+      o[gg][2 * w + 1] = __builtin_amdgcn_fdot2_f32_bf16(pk[gg], hi, o[gg][2 * w + 1], false);
+    }
+  }
+}
+
+// 128-bit raw buffer load with the nontemporal hint (each K/V byte is read once per
+// call); offsets at or past the resource's byte count read as zero without touching
+// memory.
+constexpr int kCachePolicyNT = 2;
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCachePolicyNT));
+}
+constexpr int kRsrcWord3 = 0x00020000;      // raw (untyped) buffer, gfx9-family descriptor
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
 // Selected-token count of a unit and its chunk count (identical in both kernels).
 struct UnitSpan {
   int T, cnt, N, nchunks;
+  int clen;    // tokens per chunk: N split evenly, rounded up to 16; the last chunk is shorter
 };
 
 __device__ __forceinline__ UnitSpan unit_span(const UnitInfo& ui, const int32_t* seq_lens,
@@ -114,6 +149,7 @@ __device__ __forceinline__ UnitSpan unit_span(const UnitInfo& ui, const int32_t*
   }
   s.N = N;
   s.nchunks = N > 0 ? ((N + split - 1) >> log2split) : 1;
+  s.clen = min(split, ((N + s.nchunks - 1) / s.nchunks + 15) & ~15);
   return s;
 }
 
@@ -150,8 +186,8 @@ __global__ __launch_bounds__(NT) void k_decode(
   if (chunk >= sp.nchunks) return;
   const int T = sp.T, g = ui.g, log2g = ui.log2g;
 
-  const int i0 = chunk << log2split;
-  const int i1 = min(sp.N, i0 + split);
+  const int i0 = chunk * sp.clen;
+  const int i1 = min(sp.N, i0 + sp.clen);
   // Block indices this chunk touches; entries that are not valid blocks of the unit, in
   // ascending order, become -1 (their tokens are skipped).
   const int p0 = i0 >> log2g;
@@ -174,7 +210,7 @@ __global__ __launch_bounds__(NT) void k_decode(
 #pragma unroll
   for (int gg = 0; gg < G; ++gg) qv[gg] = *reinterpret_cast<const uint4*>(qrow + (size_t)gg * D);
 
-  float m[G], l[G], o[G][EPL];
+  float m[G], l[G], o[G][EPL == 8 ? 8 : EPL];
 #pragma unroll
   for (int gg = 0; gg < G; ++gg) {
     m[gg] = kNegBig;
@@ -183,30 +219,36 @@ __global__ __launch_bounds__(NT) void k_decode(
     for (int e = 0; e < EPL; ++e) o[gg][e] = 0.0f;
   }
 
-  // This wave's share of the chunk.
-  const int per_wave = split / NWAVES;
+  // This wave's share of the chunk (a multiple of STEP tokens).
+  const int per_wave = ((sp.clen + NWAVES * STEP - 1) / (NWAVES * STEP)) * STEP;
   const int w0 = i0 + wave * per_wave;
   const int w1 = min(i1, w0 + per_wave);
-  const E* Kb = K + unit_rows * D + li * EPL;
-  const E* Vb = V + unit_rows * D + li * EPL;
+  // The unit's rows [0, T) of K and V as buffer resources: rows past T, and masked
+  // token slots (sent to kOutOfRange), read as zeros with no memory access.
+  constexpr uint32_t kRowBytes = D * sizeof(E);
+  const uint32_t nbytes = (uint32_t)T * kRowBytes;
+  const __amdgpu_buffer_rsrc_t rk =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(K + unit_rows * D), 0, (int)nbytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rv =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(V + unit_rows * D), 0, (int)nbytes, kRsrcWord3);
+  const uint32_t lane_off = (uint32_t)li * 16u;
 
   auto load_step = [&](int base, uint4* kr, uint4* vr, bool* ok) {
+    // Block indices first (independent LDS reads), then all 2U buffer loads.
+    int jb[U];
 #pragma unroll
     for (int uu = 0; uu < U; ++uu) {
       const int i = base + uu * TPW + lg;
-      int row = -1;
-      if (i < w1) {
-        const int jb = L.blk[(i >> log2g) - p0];
-        row = jb * g + (i & (g - 1));
-      }
-      ok[uu] = row >= 0 && row < T;
-      if (ok[uu]) {
-        kr[uu] = *reinterpret_cast<const uint4*>(Kb + (size_t)row * D);
-        vr[uu] = *reinterpret_cast<const uint4*>(Vb + (size_t)row * D);
-      } else {
-        kr[uu] = make_uint4(0, 0, 0, 0);
-        vr[uu] = make_uint4(0, 0, 0, 0);
-      }
+      jb[uu] = L.blk[max(0, min((i >> log2g) - p0, np - 1))];
+    }
+#pragma unroll
+    for (int uu = 0; uu < U; ++uu) {
+      const int i = base + uu * TPW + lg;
+      const int row = jb[uu] * g + (i & (g - 1));
+      ok[uu] = i < w1 && jb[uu] >= 0 && row < T;
+      const uint32_t off = ok[uu] ? (uint32_t)row * kRowBytes + lane_off : kOutOfRange;
+      kr[uu] = buffer_load16(rk, off);
+      vr[uu] = buffer_load16(rv, off);
     }
   };
 
@@ -223,43 +265,68 @@ __global__ __launch_bounds__(NT) void k_decode(
         const float t = group_sum<LPT>(s[uu][gg]) * scale_log2;
         s[uu][gg] = ok[uu] ? t : -__builtin_inff();
       }
-    float vf[U][EPL];
-#pragma unroll
-    for (int uu = 0; uu < U; ++uu) unpack(vr[uu], vf[uu], (E*)nullptr);
+    // Rescale o and l only when some running max of the wave grew (a wave-uniform
+    // branch); otherwise every alpha would be exactly 1.
+    float mx[G];
+    bool grow = false;
 #pragma unroll
     for (int gg = 0; gg < G; ++gg) {
-      float mx = m[gg];
+      mx[gg] = m[gg];
 #pragma unroll
-      for (int uu = 0; uu < U; ++uu) mx = fmaxf(mx, s[uu][gg]);
-      const float alpha = __builtin_amdgcn_exp2f(m[gg] - mx);
-      m[gg] = mx;
-      float lsum = l[gg] * alpha;
+      for (int uu = 0; uu < U; ++uu) mx[gg] = fmaxf(mx[gg], s[uu][gg]);
+      grow |= mx[gg] > m[gg];
+    }
+    if (__builtin_expect(__builtin_amdgcn_ballot_w64(grow) != 0, 0)) {
+      // Keep this a branch: if-converting it would run the rescale every step.
+      asm volatile("" ::: "memory");
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) o[gg][e] *= alpha;
+      for (int gg = 0; gg < G; ++gg) {
+        const float alpha = __builtin_amdgcn_exp2f(m[gg] - mx[gg]);
+        m[gg] = mx[gg];
+        l[gg] *= alpha;
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[gg][e] *= alpha;
+      }
+    }
+    float p[U][G];
+#pragma unroll
+    for (int uu = 0; uu < U; ++uu)
+#pragma unroll
+      for (int gg = 0; gg < G; ++gg) {
+        p[uu][gg] = __builtin_amdgcn_exp2f(s[uu][gg] - m[gg]);
+        l[gg] += p[uu][gg];
+      }
+    if constexpr (sizeof(E) == 2) {
+      static_assert(U % 2 == 0, "token pairs");
+#pragma unroll
+      for (int uu = 0; uu < U; uu += 2) pv_pair<G>(p[uu], p[uu + 1], vr[uu], vr[uu + 1], o);
+    } else {
 #pragma unroll
       for (int uu = 0; uu < U; ++uu) {
-        const float p = __builtin_amdgcn_exp2f(s[uu][gg] - mx);
-        lsum += p;
+        float vf[EPL];
+        unpack(vr[uu], vf, (E*)nullptr);
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) o[gg][e] = fmaf(p, vf[uu][e], o[gg][e]);
+        for (int gg = 0; gg < G; ++gg)
+#pragma unroll
+          for (int e = 0; e < EPL; ++e) o[gg][e] = fmaf(p[uu][gg], vf[e], o[gg][e]);
       }
-      l[gg] = lsum;
     }
   };
 
-  // Register double buffering: the loads of step n+1 are in flight while step n computes.
+  // Register double buffering: the loads of step n+1 are in flight while step n
+  // computes.  The loads are issued unconditionally (slots past w1 are out of range and
+  // cost no memory traffic) so the count of outstanding loads is the same on every path
+  // and each compute waits only for its own step's loads.
   uint4 kA[U], vA[U], kB[U], vB[U];
   bool okA[U], okB[U];
-  int base = w0;
-  if (base < w1) load_step(base, kA, vA, okA);
-  while (base < w1) {
-    if (base + STEP < w1) load_step(base + STEP, kB, vB, okB);
-    compute_step(kA, vA, okA);
-    base += STEP;
-    if (base >= w1) break;
-    if (base + STEP < w1) load_step(base + STEP, kA, vA, okA);
-    compute_step(kB, vB, okB);
-    base += STEP;
+  if (w0 < w1) {
+    load_step(w0, kA, vA, okA);
+    for (int base = w0; base < w1; base += 2 * STEP) {
+      load_step(base + STEP, kB, vB, okB);
+      compute_step(kA, vA, okA);
+      load_step(base + 2 * STEP, kA, vA, okA);
+      if (base + STEP < w1) compute_step(kB, vB, okB);
+    }
   }
 
   // Merge the lane groups of the wave (partners differ in the lane bits above LPT).

@@ -115,7 +115,8 @@ typedef struct {
   int32_t num_q_heads;     /* Hq, a multiple of num_kv_heads with G = Hq/Hkv in [1, 8] */
   int32_t num_kv_heads;    /* Hkv >= 1 */
   int32_t head_dim;        /* d: 64 or 128 */
-  int32_t t_cap;           /* tokens of capacity per unit, 1 .. 2^24 */
+  int32_t t_cap;           /* tokens of capacity per unit, 1 .. 2^24, with t_cap * head_dim *
+                              sizeof(elem) < 2^31 (else FX_E_UNSUPPORTED) */
   int32_t dtype;           /* FX_F32 or FX_BF16: element type of q, K, V, summaries, out */
   int32_t split_tokens;    /* split-K chunk in tokens (a power of two, 64..2048), 0 = automatic */
 } fx_plan_desc;
