@@ -160,6 +160,11 @@ fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_pl
   size_t off = 0;
   p->ws_scores_off = off;
   off += align_up((size_t)(p->any_scored ? p->total_blocks : 0) * 4, 256);
+  const bool topk_in_lds = fx::topk_lds_bytes(p) <= fx::kTopkLdsLimit;
+  p->ws_keys_off = off;
+  off += align_up(topk_in_lds ? 0 : (size_t)p->total_blocks * 4, 256);
+  p->ws_bits_off = off;
+  off += align_up(topk_in_lds ? 0 : (size_t)p->mask_words * 3 * 4, 256);
   p->ws_part_o_off = off;
   off += align_up((size_t)units * p->max_chunks * p->G * d * 4, 256);
   p->ws_part_ml_off = off;
@@ -273,8 +278,10 @@ fx_status fx_select(fx_plan_t p, const void* q, const void* summaries, const flo
       hipError_t e = fx::launch_score(p, q, summaries, seq_lens, scores, stream);
       if (e != hipSuccess) return FX_E_HIP;
     }
+    char* ws = static_cast<char*>(workspace);
     return hip_status(fx::launch_topk(p, scores, evict_logits, evicted_mask, seq_lens, sel_idx,
-                                      sel_cnt, stream));
+                                      sel_cnt, reinterpret_cast<uint32_t*>(ws + p->ws_keys_off),
+                                      reinterpret_cast<uint32_t*>(ws + p->ws_bits_off), stream));
   } catch (...) {
     return FX_E_HIP;
   }

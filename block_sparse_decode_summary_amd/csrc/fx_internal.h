@@ -17,6 +17,7 @@ constexpr int kMaxBlock = 256;        // largest block size g
 constexpr int kMaxSplit = 2048;       // largest split-K chunk (tokens)
 constexpr int kMinSplit = 64;
 constexpr int kMaxTcap = 1 << 24;
+constexpr size_t kTopkLdsLimit = 64 * 1024;   // larger per-unit key sets live in the workspace
 
 // Per-unit policy as the kernels read it (device table owned by the plan).
 struct UnitInfo {
@@ -64,6 +65,8 @@ struct fx_plan {
 
   // workspace layout (byte offsets)
   size_t ws_scores_off = 0;      // float [total_blocks]
+  size_t ws_keys_off = 0;        // uint32 [total_blocks]     (top-k keys when not in LDS)
+  size_t ws_bits_off = 0;        // uint32 [3 * mask_words]   (top-k bitmaps when not in LDS)
   size_t ws_part_o_off = 0;      // float [units][max_chunks][G][d]
   size_t ws_part_ml_off = 0;     // float2 [units][max_chunks][G]  (m, l)
   size_t ws_total = 0;
@@ -79,7 +82,9 @@ hipError_t launch_score(const fx_plan* p, const void* q, const void* summaries,
                         const int32_t* seq_lens, float* scores, hipStream_t stream);
 hipError_t launch_topk(const fx_plan* p, const float* scores, const float* logits,
                        uint32_t* mask, const int32_t* seq_lens, int32_t* sel_idx,
-                       int32_t* sel_cnt, hipStream_t stream);
+                       int32_t* sel_cnt, uint32_t* ws_keys, uint32_t* ws_bits,
+                       hipStream_t stream);
+size_t topk_lds_bytes(const fx_plan* p);
 hipError_t launch_decode(const fx_plan* p, const void* q, const void* K, const void* V,
                          const int32_t* seq_lens, const int32_t* sel_idx,
                          const int32_t* sel_cnt, float softmax_scale, void* out, float* lse,

@@ -32,7 +32,9 @@
 // otherwise each chunk writes its unnormalised (o, m, l).
 //
 // k_combine (one workgroup per unit with more than one chunk) merges the chunk
-// partials in chunk order, so results do not depend on scheduling.  The kernel
+// partials: per query row the max M and the weighted sum L come from workgroup
+// reductions in a fixed order, the per-chunk weights 2^(m_k - M) sit in LDS, and each
+// output sums its chunks in chunk order, so results do not depend on scheduling.  The kernel
 // boundary makes every chunk's partial visible to it; no fence is needed inside
 // k_decode (an agent-scope fence per workgroup would write back the L2 each time).
 #include "fx_device.h"
@@ -387,6 +389,32 @@ __global__ __launch_bounds__(NT) void k_decode(
   }
 }
 
+// Reductions over the 256 threads of a workgroup (lds: NWAVES floats).
+__device__ __forceinline__ float block_max(float x, float* lds) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
+  if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = x;
+  __syncthreads();
+  float r = lds[0];
+#pragma unroll
+  for (int w = 1; w < NWAVES; ++w) r = fmaxf(r, lds[w]);
+  __syncthreads();
+  return r;
+}
+__device__ __forceinline__ float block_sum_f(float x, float* lds) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
+  if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = x;
+  __syncthreads();
+  float r = 0.0f;
+#pragma unroll
+  for (int w = 0; w < NWAVES; ++w) r += lds[w];   // fixed order: deterministic
+  __syncthreads();
+  return r;
+}
+
+constexpr int kCombineTile = 256;   // chunks whose weights sit in LDS at a time
+
 template <typename E, int D, int G>
 __global__ __launch_bounds__(NT) void k_combine(
     const UnitInfo* __restrict__ units, const int32_t* __restrict__ seq_lens,
@@ -394,27 +422,73 @@ __global__ __launch_bounds__(NT) void k_combine(
     E* __restrict__ out, float* __restrict__ lse, const float* __restrict__ part_o,
     const float2* __restrict__ part_ml, uint32_t* __restrict__ err, int Hkv, int t_cap,
     int max_sel, int split, int log2split, int max_chunks) {
+  constexpr int OUTS = (G * D + NT - 1) / NT;   // outputs per thread
+  __shared__ float red[NWAVES];
+  __shared__ float Mg[G], Lg[G];
+  __shared__ float wts[kCombineTile][G];
   const int u = blockIdx.x;
   const UnitInfo ui = units[u];
   const int b = u / Hkv, h = u % Hkv;
   const UnitSpan sp = unit_span(ui, seq_lens, sel_idx + (size_t)u * max_sel, sel_cnt, u, b,
                                 t_cap, max_sel, split, log2split, max_chunks, err);
   if (sp.nchunks == 1) return;   // k_decode already wrote this unit
-  const size_t ubase = (size_t)u * max_chunks;
-  for (int idx = threadIdx.x; idx < G * D; idx += NT) {
-    const int gg = idx / D, c = idx % D;
-    float M = kNegBig;
-    for (int k = 0; k < sp.nchunks; ++k) M = fmaxf(M, part_ml[(ubase + k) * G + gg].x);
-    float Ls = 0.0f, Os = 0.0f;
-    for (int k = 0; k < sp.nchunks; ++k) {
-      const float2 ml = part_ml[(ubase + k) * G + gg];
-      const float a = __builtin_amdgcn_exp2f(ml.x - M);
-      Ls = fmaf(ml.y, a, Ls);
-      Os = fmaf(part_o[((ubase + k) * G + gg) * D + c], a, Os);
+  const int nk = sp.nchunks;
+  const float2* ml = part_ml + (size_t)u * max_chunks * G;
+  const float* po = part_o + (size_t)u * max_chunks * G * D;
+
+  // Per query row: M = max over chunks of m, L = sum over chunks of l * 2^(m - M).
+  for (int gg = 0; gg < G; ++gg) {
+    float mx = kNegBig;
+    for (int k = threadIdx.x; k < nk; k += NT) mx = fmaxf(mx, ml[(size_t)k * G + gg].x);
+    const float M = block_max(mx, red);
+    float ls = 0.0f;
+    for (int k = threadIdx.x; k < nk; k += NT) {
+      const float2 v = ml[(size_t)k * G + gg];
+      ls += v.y * __builtin_amdgcn_exp2f(v.x - M);
     }
-    const size_t orow = (size_t)b * Hkv * G + (size_t)h * G + gg;
-    store_elem(out + orow * D + c, Ls > 0.0f ? Os / Ls : 0.0f);
-    if (lse && c == 0) lse[orow] = Ls > 0.0f ? (M + __log2f(Ls)) * kLn2 : -__builtin_inff();
+    const float L = block_sum_f(ls, red);
+    if (threadIdx.x == 0) {
+      Mg[gg] = M;
+      Lg[gg] = L;
+    }
+  }
+  __syncthreads();
+
+  // out = sum over chunks of o_k * 2^(m_k - M) / L, chunks taken in order.
+  float acc[OUTS];
+#pragma unroll
+  for (int j = 0; j < OUTS; ++j) acc[j] = 0.0f;
+  for (int k0 = 0; k0 < nk; k0 += kCombineTile) {
+    const int kt = min(kCombineTile, nk - k0);
+    for (int i = threadIdx.x; i < kt * G; i += NT) {
+      const int k = i / G, gg = i % G;
+      wts[k][gg] = __builtin_amdgcn_exp2f(ml[(size_t)(k0 + k) * G + gg].x - Mg[gg]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < OUTS; ++j) {
+      const int idx = threadIdx.x + j * NT;
+      if (idx < G * D) {
+        const int gg = idx / D;
+        const float* src = po + (size_t)k0 * G * D + idx;
+        float a = acc[j];
+#pragma unroll 8
+        for (int k = 0; k < kt; ++k) a = fmaf(src[(size_t)k * G * D], wts[k][gg], a);
+        acc[j] = a;
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int j = 0; j < OUTS; ++j) {
+    const int idx = threadIdx.x + j * NT;
+    if (idx < G * D) {
+      const int gg = idx / D, c = idx % D;
+      const float L = Lg[gg];
+      const size_t orow = (size_t)b * Hkv * G + (size_t)h * G + gg;
+      store_elem(out + orow * D + c, L > 0.0f ? acc[j] / L : 0.0f);
+      if (lse && c == 0) lse[orow] = L > 0.0f ? (Mg[gg] + __log2f(L)) * kLn2 : -__builtin_inff();
+    }
   }
 }
 
