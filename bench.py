@@ -74,6 +74,31 @@ def algorithmic_bytes(w, max_sel, sel_idx, sel_cnt):
     return total, decode, parts
 
 
+def decode_source_hash() -> str:
+    import hashlib
+    path = os.path.join(ROOT, "block_sparse_decode_summary_amd", "csrc", "k_decode.hip")
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per fx_sparse_decode call from the committed counter summary, or None
+    when no summary exists for this workload or the decode source changed since."""
+    path = os.path.join(ROOT, "profiles", f"k_decode_{workload}_hbm_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].rsplit(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("k_decode.hip sha256[:16]") != decode_source_hash():
+        return None
+    try:
+        return int(fields["traffic bytes per call"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(w, inp, seconds: float, seed: int = 0):
     """Time the oracle on a bounded sample of this workload's units, one step each."""
     import numpy as np
@@ -130,6 +155,8 @@ def main() -> int:
                     help="overwrite 1 GiB between steps (outside the timed events)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-reference", action="store_true",
+                    help="after timing, run one plain 1 GiB device copy (scales HBM counters)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -207,6 +234,13 @@ def main() -> int:
     if fx.fx_read_error(plan) != 0:
         raise SystemExit("device error word set during the benchmark")
 
+    if args.copy_reference:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     sel_idx = prev.sel_idx.cpu().numpy()      # the last step's selection
     sel_cnt = prev.sel_cnt.cpu().numpy()
     total_b, dec_b, parts = algorithmic_bytes(w, plan.max_selected, sel_idx, sel_cnt)
@@ -240,10 +274,12 @@ def main() -> int:
         "data": "synthetic (seeded; shapes and value distributions of the workload definition)",
         "config": shapes,
         "alg_bytes_per_step": int(total_b),
-        "roofline": {"bound": "hbm", "kernel": "k_decode (fx_sparse_decode)",
+        "roofline": {"bound": "hbm", "kernel": "fx_sparse_decode (k_decode + k_combine)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "alg_bytes_per_launch": int(dec_b), "avg_launch_us": round(dec_avg * 1e3, 2)},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(w.name),
+                     "alg_bytes_per_launch": int(dec_b), "avg_launch_us": round(dec_avg * 1e3, 2),
+                     "k_decode_sha256_16": decode_source_hash()},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
