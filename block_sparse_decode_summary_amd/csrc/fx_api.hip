@@ -134,7 +134,12 @@ fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_pl
     const int64_t tok = std::min<int64_t>(ms * q.block, desc->t_cap);
     work += tok;
     max_tok = std::max(max_tok, tok);
-    if (q.mode != FX_STREAMING) p->any_scored = true;
+    if (q.mode != FX_STREAMING) {
+      p->any_scored = true;
+      p->host_scored.push_back(u);
+      p->max_scored_n_full_cap =
+          std::max<int32_t>(p->max_scored_n_full_cap, (int32_t)(desc->t_cap / q.block));
+    }
     if (q.mode == FX_NOSA && q.k_evict > 0) p->needs_logits = true;
   }
   if (moff > INT32_MAX || max_sel > INT32_MAX / 2) {
@@ -160,11 +165,11 @@ fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_pl
   size_t off = 0;
   p->ws_scores_off = off;
   off += align_up((size_t)(p->any_scored ? p->total_blocks : 0) * 4, 256);
-  const bool topk_in_lds = fx::topk_lds_bytes(p) <= fx::kTopkLdsLimit;
+  const bool topk_regs = fx::topk_in_registers(p);
   p->ws_keys_off = off;
-  off += align_up(topk_in_lds ? 0 : (size_t)p->total_blocks * 4, 256);
+  off += align_up(topk_regs ? 0 : (size_t)p->total_blocks * 4, 256);
   p->ws_bits_off = off;
-  off += align_up(topk_in_lds ? 0 : (size_t)p->mask_words * 3 * 4, 256);
+  off += align_up(topk_regs ? 0 : (size_t)p->mask_words * 3 * 4, 256);
   p->ws_part_o_off = off;
   off += align_up((size_t)units * p->max_chunks * p->G * d * 4, 256);
   p->ws_part_ml_off = off;
@@ -173,7 +178,8 @@ fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_pl
 
   // Device table: units | error word.
   const size_t tab_units = align_up(sizeof(UnitInfo) * units, 256);
-  const size_t tab_bytes = tab_units + 256;
+  p->n_scored = (int32_t)p->host_scored.size();
+  const size_t tab_bytes = tab_units + 256 + align_up(sizeof(int32_t) * p->host_scored.size(), 256);
   if (hipGetDevice(&p->device) != hipSuccess ||
       hipMalloc(&p->d_table, tab_bytes) != hipSuccess) {
     delete p;
@@ -182,8 +188,12 @@ fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_pl
   char* base = static_cast<char*>(p->d_table);
   p->d_units = reinterpret_cast<UnitInfo*>(base);
   p->d_error = reinterpret_cast<uint32_t*>(base + tab_units);
+  p->d_scored = reinterpret_cast<int32_t*>(base + tab_units + 256);
   if (hipMemcpy(p->d_units, p->host_units.data(), sizeof(UnitInfo) * units,
                 hipMemcpyHostToDevice) != hipSuccess ||
+      (p->n_scored > 0 &&
+       hipMemcpy(p->d_scored, p->host_scored.data(), sizeof(int32_t) * p->n_scored,
+                 hipMemcpyHostToDevice) != hipSuccess) ||
       hipMemset(base + tab_units, 0, 256) != hipSuccess) {
     (void)hipFree(p->d_table);
     delete p;

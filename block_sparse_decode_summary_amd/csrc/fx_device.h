@@ -64,6 +64,18 @@ __device__ __forceinline__ uint32_t f32_key(float f, bool* nonfinite) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// ---- raw buffer loads -----------------------------------------------------------------
+
+// 128-bit raw buffer load with the nontemporal hint (for bytes read once per call);
+// offsets at or past the resource's byte count read as zero without touching memory.
+constexpr int kCachePolicyNT = 2;
+__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4,
+                            __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCachePolicyNT));
+}
+constexpr int kRsrcWord3 = 0x00020000;      // raw (untyped) buffer, gfx9-family descriptor
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
 // ---- bounds of one unit ---------------------------------------------------------------
 
 __device__ __forceinline__ int load_seq_len(const int32_t* seq_lens, int b, int t_cap,
@@ -100,6 +112,61 @@ __device__ __forceinline__ float group_sum(float x) {
   if constexpr (LPT >= 16) x += dpp_f<kRowMirror>(x);
   if constexpr (LPT >= 32) x += __shfl_xor(x, 16);
   return x;
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, true);
+}
+
+__device__ __forceinline__ uint32_t lane_value(uint32_t x, int lane) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)x, lane);
+}
+
+// Minimum / maximum / sum over the 64 lanes of a wave (wave-uniform result).  The
+// quad permutes and the two mirrors leave every row of 16 lanes holding its row's
+// value; the four rows are then combined from lanes 0, 16, 32 and 48.
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t x) {
+  x = min(x, dpp_u32<kQuadPerm1032>(x));
+  x = min(x, dpp_u32<kQuadPerm2301>(x));
+  x = min(x, dpp_u32<kRowHalfMirror>(x));
+  x = min(x, dpp_u32<kRowMirror>(x));
+  return min(min(lane_value(x, 0), lane_value(x, 16)), min(lane_value(x, 32), lane_value(x, 48)));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x) {
+  x = max(x, dpp_u32<kQuadPerm1032>(x));
+  x = max(x, dpp_u32<kQuadPerm2301>(x));
+  x = max(x, dpp_u32<kRowHalfMirror>(x));
+  x = max(x, dpp_u32<kRowMirror>(x));
+  return max(max(lane_value(x, 0), lane_value(x, 16)), max(lane_value(x, 32), lane_value(x, 48)));
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t x) {
+  x += dpp_u32<kQuadPerm1032>(x);
+  x += dpp_u32<kQuadPerm2301>(x);
+  x += dpp_u32<kRowHalfMirror>(x);
+  x += dpp_u32<kRowMirror>(x);
+  return (lane_value(x, 0) + lane_value(x, 16)) + (lane_value(x, 32) + lane_value(x, 48));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: shifts by 1, 2, 4 and 8 inside
+// each row of 16 lanes (lanes shifted in from outside the row read 0), then the row
+// totals of lanes 15, 31 and 47 are added to the rows above them.
+__device__ __forceinline__ uint32_t wave_scan_incl_u32(uint32_t x) {
+  constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+  x += dpp_u32<kRowShr1>(x);
+  x += dpp_u32<kRowShr2>(x);
+  x += dpp_u32<kRowShr4>(x);
+  x += dpp_u32<kRowShr8>(x);
+  const int lane = threadIdx.x & 63;
+  const uint32_t r0 = lane_value(x, 15), r1 = lane_value(x, 31), r2 = lane_value(x, 47);
+  x += (lane >= 16 ? r0 : 0u) + (lane >= 32 ? r1 : 0u) + (lane >= 48 ? r2 : 0u);
+  return x;
+}
+
+// Number of set bits of a wave ballot below this lane.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t ballot) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(ballot >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)ballot, 0u));
 }
 
 // Inclusive prefix sum over the 64 lanes of a wave.

@@ -17,7 +17,7 @@ constexpr int kMaxBlock = 256;        // largest block size g
 constexpr int kMaxSplit = 2048;       // largest split-K chunk (tokens)
 constexpr int kMinSplit = 64;
 constexpr int kMaxTcap = 1 << 24;
-constexpr size_t kTopkLdsLimit = 64 * 1024;   // larger per-unit key sets live in the workspace
+constexpr int kTopkRegBlocks = 8192;   // selection keeps keys in registers up to this n_cap
 
 // Per-unit policy as the kernels read it (device table owned by the plan).
 struct UnitInfo {
@@ -46,11 +46,15 @@ struct fx_plan {
   int32_t G = 0;
   int32_t units = 0;
   std::vector<fx::UnitInfo> host_units;
+  std::vector<int32_t> host_scored;
   int device = 0;
-  // device table: [units] UnitInfo | uint32 error word
+  // device table: [units] UnitInfo | uint32 error word | [n_scored] int32 unit ids
   void* d_table = nullptr;
   fx::UnitInfo* d_units = nullptr;
   uint32_t* d_error = nullptr;
+  int32_t* d_scored = nullptr;   // retrieval and NOSA units, ascending
+  int32_t n_scored = 0;
+  int32_t max_scored_n_full_cap = 0;   // max over scored units of t_cap / g
 
   int64_t total_blocks = 0;
   int64_t mask_words = 0;
@@ -65,8 +69,8 @@ struct fx_plan {
 
   // workspace layout (byte offsets)
   size_t ws_scores_off = 0;      // float [total_blocks]
-  size_t ws_keys_off = 0;        // uint32 [total_blocks]     (top-k keys when not in LDS)
-  size_t ws_bits_off = 0;        // uint32 [3 * mask_words]   (top-k bitmaps when not in LDS)
+  size_t ws_keys_off = 0;        // uint32 [total_blocks]     (top-k keys, workspace path only)
+  size_t ws_bits_off = 0;        // uint32 [3 * mask_words]   (top-k bitmaps, workspace path only)
   size_t ws_part_o_off = 0;      // float [units][max_chunks][G][d]
   size_t ws_part_ml_off = 0;     // float2 [units][max_chunks][G]  (m, l)
   size_t ws_total = 0;
@@ -84,7 +88,7 @@ hipError_t launch_topk(const fx_plan* p, const float* scores, const float* logit
                        uint32_t* mask, const int32_t* seq_lens, int32_t* sel_idx,
                        int32_t* sel_cnt, uint32_t* ws_keys, uint32_t* ws_bits,
                        hipStream_t stream);
-size_t topk_lds_bytes(const fx_plan* p);
+bool topk_in_registers(const fx_plan* p);   // else keys and bitmaps use the workspace
 hipError_t launch_decode(const fx_plan* p, const void* q, const void* K, const void* V,
                          const int32_t* seq_lens, const int32_t* sel_idx,
                          const int32_t* sel_cnt, float softmax_scale, void* out, float* lse,

@@ -110,16 +110,6 @@ __device__ __forceinline__ void pv_pair(const float* pa, const float* pb, const 
   }
 }
 
-// 128-bit raw buffer load with the nontemporal hint (each K/V byte is read once per
-// call); offsets at or past the resource's byte count read as zero without touching
-// memory.
-constexpr int kCachePolicyNT = 2;
-__device__ __forceinline__ uint4 buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint4,
-                            __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kCachePolicyNT));
-}
-constexpr int kRsrcWord3 = 0x00020000;      // raw (untyped) buffer, gfx9-family descriptor
-constexpr uint32_t kOutOfRange = 0x80000000u;
 
 // Selected-token count of a unit and its chunk count (identical in both kernels).
 struct UnitSpan {

@@ -14,11 +14,17 @@
 // off below).  This is the group's sum of raw dot products with the summary; the fixed
 // order makes the float32 value, and hence the selection, reproducible bit for bit.
 //
-// Mapping: one wave per tile of 64 blocks of one unit.  qs goes to LDS once per
-// workgroup; the tile's summary rows are staged into LDS with 16-byte loads (row
-// stride WORDS+1 words, so lane i reading word c of row i hits bank (i + c) mod 64);
-// then lane i runs block j0 + i's d-term chain in order.  Each lane issues all of its
-// staging loads before writing any of them, so a tile costs one memory round trip.
+// Mapping: the grid covers only retrieval and NOSA units (a host-built list); one
+// 256-thread workgroup takes four consecutive 64-block tiles of a unit, one tile per
+// wave and one block per lane, and forms the float64 group sum qs once for all four.
+// Each wave requests its whole tile at once through a buffer resource bounded to the
+// unit's full blocks (rows past the end read as zero without a memory access), in
+// column-chunk order: chunk ch holds columns [ch*C, ch*C + C) of all 64 rows, C being
+// 32 words, and one load instruction covers eight 128-byte row segments.  The chunks
+// then pass one at a time through a per-wave LDS tile with stride 33 words (33 is odd,
+// so lane i reading word c of row i never shares a bank with another lane), and the
+// lane's chain continues across the chunks in column order.  Small LDS per workgroup
+// keeps several workgroups, and their loads, resident on each CU.
 #include "fx_device.h"
 
 namespace fx {
@@ -32,83 +38,105 @@ __device__ __forceinline__ double elem_f64(const uint32_t* row, int c, bf16_t*) 
   return (double)((c & 1) ? bf16_hi(w) : bf16_lo(w));
 }
 
-constexpr int kTile = 64;
+constexpr int kTile = 64;         // blocks per tile (one per lane)
+constexpr int kWaves = 4;         // tiles per workgroup (one per wave)
+constexpr int kChunkWords = 32;   // row words staged in LDS at a time
 
 template <typename E, int D>
-__global__ __launch_bounds__(64) void k_score(
-    const UnitInfo* __restrict__ units, const E* __restrict__ q, const E* __restrict__ S,
-    const int32_t* __restrict__ seq_lens, float* __restrict__ scores, uint32_t* __restrict__ err,
-    int Hkv, int G, int t_cap, int tiles_per_unit) {
-  constexpr int WORDS = D * (int)sizeof(E) / 4;
-  const int u = blockIdx.x / tiles_per_unit;
-  const int tile = blockIdx.x % tiles_per_unit;
+__global__ __launch_bounds__(kWaves * 64) void k_score(
+    const UnitInfo* __restrict__ units, const int32_t* __restrict__ scored,
+    const E* __restrict__ q, const E* __restrict__ S, const int32_t* __restrict__ seq_lens,
+    float* __restrict__ scores, uint32_t* __restrict__ err, int Hkv, int G, int t_cap,
+    int quads_per_unit) {
+  constexpr int ROW_BYTES = D * (int)sizeof(E);
+  constexpr int WORDS = ROW_BYTES / 4;                    // 32-bit words per summary row
+  constexpr int NCH = WORDS / kChunkWords;                 // column chunks per row
+  constexpr int CPIECES = kChunkWords / 4;                 // 16-byte pieces per row chunk
+  constexpr int PER_LANE = kTile * CPIECES / 64;           // pieces per lane per chunk
+  constexpr int CCOLS = kChunkWords * 4 / (int)sizeof(E);  // columns per chunk
+  constexpr int QV4 = ROW_BYTES / 16;                      // 16-byte pieces per query row
+  static_assert(WORDS % kChunkWords == 0, "row chunks");
+  const int su = blockIdx.x / quads_per_unit;
+  const int quad = blockIdx.x % quads_per_unit;
+  const int u = scored[su];
   const UnitInfo ui = units[u];
-  if (ui.mode == FX_STREAMING) return;
   const int b = u / Hkv, h = u % Hkv;
   const int T = load_seq_len(seq_lens, b, t_cap, err);
   const int n_full = T >> ui.log2g;
-  const int j0 = tile * kTile;
-  if (j0 >= n_full) return;
-  const int nrows = min(kTile, n_full - j0);
-  const int lane = threadIdx.x;
+  const int tile0 = quad * kWaves;
+  if (tile0 * kTile >= n_full) return;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int j0 = (tile0 + w) * kTile;
 
+  __shared__ uint32_t rows[kWaves][kTile][kChunkWords + 1];
+  __shared__ uint4 qrows[kMaxGroup * QV4];
   __shared__ double qs[D];
-  __shared__ uint32_t rows[kTile][WORDS + 1];
 
-  const E* qg = q + ((size_t)b * Hkv * G + (size_t)h * G) * D;
-  for (int c = lane; c < D; c += 64) {
-    double a = (double)to_f32(qg[c]);
-    for (int g = 1; g < G; ++g) a = a + (double)to_f32(qg[(size_t)g * D + c]);
+  // The whole tile, chunk by chunk: piece m = lane + 64k of chunk ch is row m / CPIECES,
+  // 16-byte piece ch*CPIECES + m % CPIECES.
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(S + (size_t)ui.block_off * D), 0, n_full * ROW_BYTES, kRsrcWord3);
+  uint4 buf[NCH][PER_LANE];
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch)
+#pragma unroll
+    for (int k = 0; k < PER_LANE; ++k) {
+      const int m = lane + 64 * k;
+      const uint32_t row = (uint32_t)(j0 + m / CPIECES);
+      buf[ch][k] = buffer_load16(rs, row * (uint32_t)ROW_BYTES +
+                                         (uint32_t)((ch * CPIECES + m % CPIECES) * 16));
+    }
+  const uint4* qsrc = reinterpret_cast<const uint4*>(q + ((size_t)b * Hkv * G + (size_t)h * G) * D);
+  const int nq = G * QV4;
+  uint4 qv = make_uint4(0, 0, 0, 0);
+  if ((int)threadIdx.x < nq) qv = qsrc[threadIdx.x];
+  if ((int)threadIdx.x < nq) qrows[threadIdx.x] = qv;
+  __syncthreads();
+  const E* qe = reinterpret_cast<const E*>(qrows);
+  if ((int)threadIdx.x < D) {
+    const int c = threadIdx.x;
+    double a = (double)to_f32(qe[c]);
+    for (int g = 1; g < G; ++g) a = a + (double)to_f32(qe[g * D + c]);
     qs[c] = a;
   }
-  // Stage the tile: every lane issues all of its 16-byte loads before the first LDS
-  // write, so the tile costs one memory round trip.
-  const uint4* src = reinterpret_cast<const uint4*>(S + ((size_t)ui.block_off + j0) * D);
-  constexpr int V4 = WORDS / 4;                 // 16-byte vectors per row
-  constexpr int PER_LANE = kTile * V4 / 64;
-  const int nvec = nrows * V4;
-  uint4 buf[PER_LANE];
-#pragma unroll
-  for (int k = 0; k < PER_LANE; ++k) {
-    const int i = lane + k * 64;
-    buf[k] = i < nvec ? src[i] : make_uint4(0, 0, 0, 0);
-  }
-#pragma unroll
-  for (int k = 0; k < PER_LANE; ++k) {
-    const int i = lane + k * 64;
-    if (i < nvec) {
-      const int r = i / V4, c = (i % V4) * 4;
-      rows[r][c + 0] = buf[k].x;
-      rows[r][c + 1] = buf[k].y;
-      rows[r][c + 2] = buf[k].z;
-      rows[r][c + 3] = buf[k].w;
-    }
-  }
-  __syncthreads();
-  if (lane >= nrows) return;
 
-  const uint32_t* row = rows[lane];
   double acc = 0.0;
-  {
+#pragma unroll
+  for (int ch = 0; ch < NCH; ++ch) {
+#pragma unroll
+    for (int k = 0; k < PER_LANE; ++k) {
+      const int m = lane + 64 * k;
+      uint32_t* dst = &rows[w][m / CPIECES][(m % CPIECES) * 4];
+      dst[0] = buf[ch][k].x;
+      dst[1] = buf[ch][k].y;
+      dst[2] = buf[ch][k].z;
+      dst[3] = buf[ch][k].w;
+    }
+    __syncthreads();
+    const uint32_t* row = rows[w][lane];
+    {
 #pragma clang fp contract(off)
 #pragma unroll 16
-    for (int c = 0; c < D; ++c) {
-      const double prod = qs[c] * elem_f64(row, c, (E*)nullptr);
-      acc = acc + prod;
+      for (int c = 0; c < CCOLS; ++c) {
+        const double prod = qs[ch * CCOLS + c] * elem_f64(row, c, (E*)nullptr);
+        acc = acc + prod;
+      }
     }
+    __syncthreads();
   }
-  scores[(size_t)ui.block_off + j0 + lane] = (float)acc;
+  if (j0 + lane < n_full) scores[(size_t)ui.block_off + j0 + lane] = (float)acc;
 }
 
 template <typename E, int D>
 hipError_t launch_t(const fx_plan* p, const void* q, const void* S, const int32_t* seq_lens,
                     float* scores, hipStream_t stream) {
-  const int tiles = (p->max_n_full_cap + kTile - 1) / kTile;
-  if (tiles == 0) return hipSuccess;
-  const dim3 grid((unsigned)((int64_t)tiles * p->units));
-  k_score<E, D><<<grid, 64, 0, stream>>>(p->d_units, static_cast<const E*>(q),
-                                         static_cast<const E*>(S), seq_lens, scores, p->d_error,
-                                         p->desc.num_kv_heads, p->G, p->desc.t_cap, tiles);
+  const int tiles = (p->max_scored_n_full_cap + kTile - 1) / kTile;
+  const int quads = (tiles + kWaves - 1) / kWaves;
+  if (quads == 0 || p->n_scored == 0) return hipSuccess;
+  const dim3 grid((unsigned)((int64_t)quads * p->n_scored));
+  k_score<E, D><<<grid, kWaves * 64, 0, stream>>>(
+      p->d_units, p->d_scored, static_cast<const E*>(q), static_cast<const E*>(S), seq_lens,
+      scores, p->d_error, p->desc.num_kv_heads, p->G, p->desc.t_cap, quads);
   return hipGetLastError();
 }
 

@@ -199,6 +199,43 @@ def test_score_ties_prefer_lower_index():
     assert list(gv.unit(0).sel) == [7, 9, 20]
 
 
+@pytest.mark.parametrize("t_cap", [8192 * 16, 8192 * 16 + 3000])
+def test_many_blocks_per_unit(t_cap):
+    """n_cap = 8192 is the largest unit whose selection keys stay in registers; one more
+    block slot sends the plan through the workspace path of the selection kernel."""
+    pols = [HeadPolicy(MODE_RETRIEVAL, block=16, sub_block=4, top_k=40, force_sink=1, force_last=1),
+            HeadPolicy(MODE_NOSA, block=16, sub_block=8, top_k=24, k_evict=48),
+            HeadPolicy(MODE_STREAMING, block=16, sub_block=16, sink_tokens=64, local_tokens=512)]
+    w = _custom(f"blocks_{t_cap}", 2, 6, 3, 64, "bf16", t_cap, [t_cap, t_cap - 7], pols * 2)
+    _run_and_compare_all(w.replace(drift=(0.9, 0.44)), steps=2)
+
+
+def test_equal_values_take_lowest_indices():
+    """Zero keys make every score +0 and zero logits tie every block, so the k best are the
+    k lowest eligible indices, with far more equal candidates than one wave ranks."""
+    g, T = 16, 16 * 3000 + 5
+    pols = [HeadPolicy(MODE_RETRIEVAL, block=g, sub_block=16, top_k=100, force_sink=1, force_last=1),
+            HeadPolicy(MODE_NOSA, block=g, sub_block=16, top_k=70, k_evict=90)]
+    w = _custom("all_ties", 1, 4, 2, 128, "bf16", T, [T], pols)
+    inp = generate(w, DEV)
+    inp.K.zero_()
+    inp.logits.zero_()
+    plan = make_plan(w)
+    bufs = fx.allocate_step_buffers(plan, DEV)
+    run_select_decode(plan, bufs, inp, inp.q)
+    gv = GpuView(plan, bufs, w)
+    n_full, n_tot = T // g, -(-T // g)
+    for u in range(2):
+        ref = oracle_unit(inp, u, inp.q)
+        compare_unit(w, u, gv, ref)
+    # retrieval: F = {0, last}; NOSA: F = {last (partial)}, Γe = 0..89, Γq = 90..159.
+    assert list(gv.unit(0).sel) == list(range(0, 101)) + [n_tot - 1]
+    assert list(gv.unit(1).sel) == list(range(0, 160)) + [n_tot - 1]
+    ev = gv.evicted(1)
+    assert not ev[:90].any() and ev[90:n_full].all() and not ev[n_full:].any()
+    assert fx.fx_read_error(plan) == 0
+
+
 def test_summary_is_rounded_once():
     """A sub-block mean just above a bfloat16 tie: one rounding gives 241/256, two give 240/256."""
     g = 16
