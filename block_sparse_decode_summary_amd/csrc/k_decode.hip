@@ -13,7 +13,12 @@
 // only the last block of a unit can be partial and selections are ascending, token i
 // lives in selected block i / g at offset i % g.  A unit's N tokens are cut into
 // nchunks = ceil(N / split) chunks of equal length (rounded up to 16 tokens), one
-// workgroup each (grid = units x max_chunks; chunks past the unit's count exit at once).
+// workgroup each (grid = units x stride, stride = max_chunks rounded up to an odd
+// number; chunks past the unit's count exit at once).  A unit's chunks are adjacent
+// workgroups, so the machine sweeps the K/V cache roughly unit by unit.  Workgroup i
+// runs on XCD i mod 8; with an odd stride the first chunk of unit u (present for every
+// unit) lands on XCD (u * stride) mod 8, which cycles through all eight XCDs, where an
+// even stride would pile the first chunks onto a few of them.
 //
 // k_decode (4 waves per chunk): a token's d-vector is spread over LPT lanes, each lane
 // holding 16 bytes (8 bfloat16 / 4 float32) of the K and V rows, so every load is a
@@ -168,8 +173,9 @@ __global__ __launch_bounds__(NT) void k_decode(
   static_assert(LPT >= 4 && LPT <= 32 && 64 % LPT == 0, "lane layout");
   __shared__ DecodeLds<E, D, G> L;
 
-  const int u = blockIdx.x / max_chunks;
-  const int chunk = blockIdx.x % max_chunks;
+  const int stride = max_chunks | 1;
+  const int u = blockIdx.x / stride;
+  const int chunk = blockIdx.x % stride;
   const UnitInfo ui = units[u];
   const int b = u / Hkv, h = u % Hkv;
   const int32_t* sel = sel_idx + (size_t)u * max_sel;
@@ -489,7 +495,7 @@ hipError_t launch_t(const fx_plan* p, const void* q, const void* K, const void* 
                     hipStream_t stream) {
   constexpr int U = 4;
   const int Hkv = p->desc.num_kv_heads, t_cap = p->desc.t_cap;
-  const dim3 grid((unsigned)((int64_t)p->units * p->max_chunks));
+  const dim3 grid((unsigned)((int64_t)p->units * (p->max_chunks | 1)));
   k_decode<E, D, G, U><<<grid, NT, 0, stream>>>(
       p->d_units, static_cast<const E*>(q), static_cast<const E*>(K), static_cast<const E*>(V),
       seq_lens, sel_idx, sel_cnt, softmax_scale * kLog2e, static_cast<E*>(out), lse, part_o,

@@ -17,6 +17,9 @@
 // Mapping: the grid covers only retrieval and NOSA units (a host-built list); one
 // 256-thread workgroup takes four consecutive 64-block tiles of a unit, one tile per
 // wave and one block per lane, and forms the float64 group sum qs once for all four.
+// The unit index varies fastest along the grid: workgroup i runs on XCD i mod 8, so
+// this spreads the first tile groups (present for every unit) over all eight XCDs
+// instead of stacking them on one.
 // Each wave requests its whole tile at once through a buffer resource bounded to the
 // unit's full blocks (rows past the end read as zero without a memory access), in
 // column-chunk order: chunk ch holds columns [ch*C, ch*C + C) of all 64 rows, C being
@@ -56,8 +59,9 @@ __global__ __launch_bounds__(kWaves * 64) void k_score(
   constexpr int CCOLS = kChunkWords * 4 / (int)sizeof(E);  // columns per chunk
   constexpr int QV4 = ROW_BYTES / 16;                      // 16-byte pieces per query row
   static_assert(WORDS % kChunkWords == 0, "row chunks");
-  const int su = blockIdx.x / quads_per_unit;
-  const int quad = blockIdx.x % quads_per_unit;
+  const int n_su = gridDim.x / quads_per_unit;
+  const int quad = blockIdx.x / n_su;
+  const int su = blockIdx.x % n_su;
   const int u = scored[su];
   const UnitInfo ui = units[u];
   const int b = u / Hkv, h = u % Hkv;
