@@ -105,7 +105,7 @@ fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_pl
   p->G = desc->num_q_heads / desc->num_kv_heads;
   p->units = units;
   p->host_units.resize(units);
-  int64_t boff = 0, moff = 0, max_sel = 1, max_ncap = 0, max_nfull = 0, work = 0, max_tok = 1;
+  int64_t boff = 0, moff = 0, max_sel = 1, max_ncap = 0, max_nfull = 0, work = 0;
   for (int u = 0; u < units; ++u) {
     const fx_head_policy& q = pol[u];
     UnitInfo& ui = p->host_units[u];
@@ -133,7 +133,6 @@ fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_pl
     max_nfull = std::max<int64_t>(max_nfull, desc->t_cap / q.block);
     const int64_t tok = std::min<int64_t>(ms * q.block, desc->t_cap);
     work += tok;
-    max_tok = std::max(max_tok, tok);
     if (q.mode != FX_STREAMING) {
       p->any_scored = true;
       p->host_scored.push_back(u);
@@ -152,14 +151,17 @@ fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_pl
   p->max_n_cap = (int32_t)max_ncap;
   p->max_n_full_cap = (int32_t)max_nfull;
 
-  int64_t split = desc->split_tokens;
-  if (split == 0) {
-    split = 256;
-    while (split < 1024 && split * 2 * 4096 <= work) split *= 2;
+  // Selected tokens of all units, laid end to end, are indexed with 32-bit integers.
+  if (work > INT32_MAX) {
+    delete p;
+    return FX_E_UNSUPPORTED;
   }
-  p->split = (int32_t)split;
-  p->log2split = log2i(split);
-  p->max_chunks = (int32_t)ceil_div(max_tok, split);
+  p->split = desc->split_tokens != 0 ? desc->split_tokens : fx::kAutoSplit;
+  p->decode_grid = fx::decode_grid(p);
+  if (p->decode_grid <= 0) {
+    delete p;
+    return FX_E_HIP;
+  }
 
   const int d = desc->head_dim;
   size_t off = 0;
@@ -170,10 +172,13 @@ fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_pl
   off += align_up(topk_regs ? 0 : (size_t)p->total_blocks * 4, 256);
   p->ws_bits_off = off;
   off += align_up(topk_regs ? 0 : (size_t)p->mask_words * 3 * 4, 256);
+  const size_t slots = (size_t)p->decode_grid * 2;   // head and tail piece per segment
   p->ws_part_o_off = off;
-  off += align_up((size_t)units * p->max_chunks * p->G * d * 4, 256);
+  off += align_up(slots * p->G * d * 4, 256);
   p->ws_part_ml_off = off;
-  off += align_up((size_t)units * p->max_chunks * p->G * 8, 256);
+  off += align_up(slots * p->G * 8, 256);
+  p->ws_seg_off = off;
+  off += align_up((size_t)p->decode_grid * 8, 256);
   p->ws_total = std::max<size_t>(off, 256);
 
   // Device table: units | error word.
@@ -311,7 +316,8 @@ fx_status fx_sparse_decode(fx_plan_t p, const void* q, const void* K, const void
     char* ws = static_cast<char*>(workspace);
     return hip_status(fx::launch_decode(p, q, K, V, seq_lens, sel_idx, sel_cnt, softmax_scale, out,
                                         lse, reinterpret_cast<float*>(ws + p->ws_part_o_off),
-                                        reinterpret_cast<float*>(ws + p->ws_part_ml_off), stream));
+                                        reinterpret_cast<float*>(ws + p->ws_part_ml_off),
+                                        reinterpret_cast<int32_t*>(ws + p->ws_seg_off), stream));
   } catch (...) {
     return FX_E_HIP;
   }

@@ -14,8 +14,10 @@ namespace fx {
 
 constexpr int kMaxGroup = 8;          // G = Hq / Hkv
 constexpr int kMaxBlock = 256;        // largest block size g
-constexpr int kMaxSplit = 2048;       // largest split-K chunk (tokens)
+constexpr int kMaxSplit = 2048;       // largest minimum decode segment; also the token run
+                                      // whose block indices one LDS list holds
 constexpr int kMinSplit = 64;
+constexpr int kAutoSplit = 256;       // minimum decode segment when the caller passes 0
 constexpr int kMaxTcap = 1 << 24;
 constexpr int kTopkRegBlocks = 8192;   // selection keeps keys in registers up to this n_cap
 
@@ -61,9 +63,8 @@ struct fx_plan {
   int32_t max_sel = 0;
   int32_t max_n_cap = 0;
   int32_t max_n_full_cap = 0;    // max over units of t_cap / g
-  int32_t split = 0;             // split-K chunk in tokens (power of two)
-  int32_t log2split = 0;
-  int32_t max_chunks = 0;        // chunks per unit, upper bound
+  int32_t split = 0;             // minimum decode segment in tokens (power of two)
+  int32_t decode_grid = 0;       // decode workgroups = decode segments
   bool any_scored = false;       // some unit is retrieval or NOSA
   bool needs_logits = false;     // some NOSA unit has k_evict > 0
 
@@ -71,8 +72,9 @@ struct fx_plan {
   size_t ws_scores_off = 0;      // float [total_blocks]
   size_t ws_keys_off = 0;        // uint32 [total_blocks]     (top-k keys, workspace path only)
   size_t ws_bits_off = 0;        // uint32 [3 * mask_words]   (top-k bitmaps, workspace path only)
-  size_t ws_part_o_off = 0;      // float [units][max_chunks][G][d]
-  size_t ws_part_ml_off = 0;     // float2 [units][max_chunks][G]  (m, l)
+  size_t ws_part_o_off = 0;      // float [decode_grid][2][G][d]   (head, tail pieces)
+  size_t ws_part_ml_off = 0;     // float2 [decode_grid][2][G]     (m, l)
+  size_t ws_seg_off = 0;         // int2 [decode_grid]             (unit, pieces)
   size_t ws_total = 0;
 };
 
@@ -92,7 +94,8 @@ bool topk_in_registers(const fx_plan* p);   // else keys and bitmaps use the wor
 hipError_t launch_decode(const fx_plan* p, const void* q, const void* K, const void* V,
                          const int32_t* seq_lens, const int32_t* sel_idx,
                          const int32_t* sel_cnt, float softmax_scale, void* out, float* lse,
-                         float* part_o, float* part_ml, hipStream_t stream);
+                         float* part_o, float* part_ml, int32_t* seg_rec, hipStream_t stream);
+int decode_grid(const fx_plan* p);   // resident decode workgroups on the current device (0: error)
 hipError_t launch_delta(const fx_plan* p, const int32_t* prev_idx, const int32_t* prev_cnt,
                         const int32_t* cur_idx, const int32_t* cur_cnt, int32_t* added,
                         int32_t* added_cnt, int32_t* removed, int32_t* removed_cnt,

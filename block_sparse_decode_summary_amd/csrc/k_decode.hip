@@ -11,37 +11,47 @@
 //   out = sum_t e^{s_t - m} V_t / l,  l = sum_t e^{s_t - m},  lse = m + ln l.
 // The selected tokens of a unit are numbered i = 0 .. N-1 in ascending order; because
 // only the last block of a unit can be partial and selections are ascending, token i
-// lives in selected block i / g at offset i % g.  A unit's N tokens are cut into
-// nchunks = ceil(N / split) chunks of equal length (rounded up to 16 tokens), one
-// workgroup each (grid = units x stride, stride = max_chunks rounded up to an odd
-// number; chunks past the unit's count exit at once).  A unit's chunks are adjacent
-// workgroups, so the machine sweeps the K/V cache roughly unit by unit.  Workgroup i
-// runs on XCD i mod 8; with an odd stride the first chunk of unit u (present for every
-// unit) lands on XCD (u * stride) mod 8, which cycles through all eight XCDs, where an
-// even stride would pile the first chunks onto a few of them.
+// lives in selected block i / g at offset i % g.
 //
-// k_decode (4 waves per chunk): a token's d-vector is spread over LPT lanes, each lane
-// holding 16 bytes (8 bfloat16 / 4 float32) of the K and V rows, so every load is a
-// 128-bit load and each wave instruction reads 64/LPT whole rows.  K and V are read
-// through raw buffer resources bounded to the unit's T valid rows: masked token slots
-// get an out-of-range offset and read zeros without a branch or a memory access.
-// Loads for the next step of U tokens per lane group are issued before the current
-// step is computed (register double buffering), so two steps are in flight per wave.
-// Each lane keeps the G query rows' matching 16 bytes in registers, forms G partial
-// dot products (v_dot2_f32_bf16 for bfloat16) and DPP-reduces them across its LPT
-// lanes.  The online softmax runs in base 2 (scores pre-multiplied by scale*log2(e))
-// per lane group, rescaling o and l only in steps where some running max grew.  For
-// bfloat16 the P.V update takes tokens in pairs: p is rounded to bfloat16 and one
-// v_dot2_f32_bf16 per (row, column) accumulates both tokens.  Lane groups, then waves,
-// merge with the log-sum-exp rule.  A unit with one chunk writes `out` directly;
-// otherwise each chunk writes its unnormalised (o, m, l).
+// Work split (stream-K): the units' token ranges, laid end to end in unit order, form
+// one sequence of `total` tokens, cut into equal segments of S = max(ceil(total / P),
+// split) tokens, P being the number of workgroups that fit on the device at once.  The
+// grid has exactly P workgroups, all resident; workgroup s streams segment s, which may
+// cover the end of one unit, whole units, and the start of another.  Every workgroup
+// first scans all units (selected-token count N_u from seq_lens, sel_cnt and the last
+// selected block) for the prefix sums; that costs a few dependent loads once per
+// workgroup instead of once per chunk, and equal segments leave no tail of late chunks
+// and no imbalance between XCDs.  A unit that lies inside one segment is finished by
+// that workgroup.  A unit that crosses segment boundaries leaves one partial (o, m, l)
+// per segment it touches: in its first segment in slot 1 ("tail") of that segment, in
+// later ones in slot 0 ("head"); its first segment also records (unit, piece count).
+// Units with no tokens (N_u = 0) get out = 0 and lse = -inf from workgroup u mod P.
 //
-// k_combine (one workgroup per unit with more than one chunk) merges the chunk
-// partials: per query row the max M and the weighted sum L come from workgroup
-// reductions in a fixed order, the per-chunk weights 2^(m_k - M) sit in LDS, and each
-// output sums its chunks in chunk order, so results do not depend on scheduling.  The kernel
-// boundary makes every chunk's partial visible to it; no fence is needed inside
-// k_decode (an agent-scope fence per workgroup would write back the L2 each time).
+// k_decode (4 waves per workgroup): within a piece of a unit, tokens go through LDS
+// lists of at most kMaxSplit tokens' block indices; each list is shared out to the four
+// waves in equal runs.  A token's d-vector is spread over LPT lanes, each lane holding
+// 16 bytes (8 bfloat16 / 4 float32) of the K and V rows, so every load is a 128-bit
+// load and each wave instruction reads 64/LPT whole rows.  K and V are read through raw
+// buffer resources bounded to the unit's T valid rows: masked token slots get an
+// out-of-range offset and read zeros without a branch or a memory access.  Loads for
+// the next step of U tokens per lane group are issued before the current step is
+// computed (register double buffering), so two steps are in flight per wave.  Each lane
+// keeps the G query rows' matching 16 bytes in registers, forms G partial dot products
+// (v_dot2_f32_bf16 for bfloat16) and DPP-reduces them across its LPT lanes.  The online
+// softmax runs in base 2 (scores pre-multiplied by scale*log2(e)) per lane group,
+// rescaling o and l only in steps where some running max grew.  For bfloat16 the P.V
+// update takes tokens in pairs: p is rounded to bfloat16 and one v_dot2_f32_bf16 per
+// (row, column) accumulates both tokens.  Lane groups, then waves, merge with the
+// log-sum-exp rule.
+//
+// k_combine (one workgroup per segment, exits unless the segment recorded a unit that
+// continues past it) merges that unit's partials in segment order with the
+// log-sum-exp rule, each output on its own thread in a fixed order, so results do not
+// depend on scheduling.  The kernel boundary makes every partial visible to
+// it; no fence is needed inside k_decode (an agent-scope fence per workgroup would
+// write back the L2 each time).
+#include <type_traits>
+
 #include "fx_device.h"
 
 namespace fx {
@@ -116,47 +126,76 @@ __device__ __forceinline__ void pv_pair(const float* pa, const float* pb, const 
 }
 
 
-// Selected-token count of a unit and its chunk count (identical in both kernels).
-struct UnitSpan {
-  int T, cnt, N, nchunks;
-  int clen;    // tokens per chunk: N split evenly, rounded up to 16; the last chunk is shorter
+// Selected-token count of unit u: N = (cnt - 1) * g + the valid tokens of the last
+// selected block (0 when cnt == 0).  seq_lens and sel_cnt outside their ranges are
+// clamped and, when `report`, flagged.
+struct UnitTokens {
+  int T, N;
 };
 
-__device__ __forceinline__ UnitSpan unit_span(const UnitInfo& ui, const int32_t* seq_lens,
-                                              const int32_t* sel, const int32_t* sel_cnt, int u,
-                                              int b, int t_cap, int max_sel, int split,
-                                              int log2split, int max_chunks, uint32_t* err) {
-  UnitSpan s;
-  s.T = load_seq_len(seq_lens, b, t_cap, err);
+__device__ __forceinline__ UnitTokens unit_tokens(const UnitInfo* units, const int32_t* seq_lens,
+                                                  const int32_t* sel_idx, const int32_t* sel_cnt,
+                                                  int u, int Hkv, int t_cap, int max_sel,
+                                                  bool report, uint32_t* err) {
+  const int g = units[u].g;
+  int T = seq_lens[u / Hkv];
   int cnt = sel_cnt[u];
+  if (T < 0 || T > t_cap) {
+    if (report) atomicOr(err, (uint32_t)FX_ERR_SEQ_LEN);
+    T = T < 0 ? 0 : t_cap;
+  }
   if (cnt < 0 || cnt > max_sel) {
-    if (threadIdx.x == 0) atomicOr(err, (uint32_t)FX_ERR_SEL_COUNT);
+    if (report) atomicOr(err, (uint32_t)FX_ERR_SEL_COUNT);
     cnt = cnt < 0 ? 0 : max_sel;
   }
-  s.cnt = cnt;
   int N = 0;
   if (cnt > 0) {
-    const int last = sel[cnt - 1];
-    const int valid_last = min(max(s.T - last * ui.g, 0), ui.g);
-    N = (cnt - 1) * ui.g + valid_last;
+    const int64_t last = sel_idx[(size_t)u * max_sel + cnt - 1];
+    const int64_t valid_last = min(max((int64_t)T - last * g, (int64_t)0), (int64_t)g);
+    N = (cnt - 1) * g + (int)valid_last;
   }
-  if (N > max_chunks * split) {   // only for selections that are not valid for this unit
-    if (threadIdx.x == 0) atomicOr(err, (uint32_t)FX_ERR_SEL_INDEX);
-    N = max_chunks * split;
-  }
-  s.N = N;
-  s.nchunks = N > 0 ? ((N + split - 1) >> log2split) : 1;
-  s.clen = min(split, ((N + s.nchunks - 1) / s.nchunks + 15) & ~15);
-  return s;
+  return {T, N};
 }
 
 template <typename E, int D, int G>
 struct DecodeLds {
-  int blk[kMaxSplit + 1];          // selected block indices covering this chunk
+  int blk[kMaxSplit + 1];          // selected block indices of the current token run
   float o[NWAVES][G][D];
   float m[NWAVES][G];
   float l[NWAVES][G];
+  int scan[2][NWAVES];
+  int first_unit, first_pos;
 };
+
+constexpr int kScanKeep = 4;       // unit chunks (NT units each) kept in registers between scans
+
+// Inclusive prefix sum over the workgroup (slot: NWAVES ints, written then read after one
+// barrier; alternate slots between consecutive calls).
+__device__ __forceinline__ int block_incl_scan(int x, int* slot, int* total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int incl = (int)wave_scan_incl_u32((uint32_t)x);
+  if (lane == 63) slot[w] = incl;
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < NWAVES; ++i) {
+    const int v = slot[i];
+    off += i < w ? v : 0;
+    tot += v;
+  }
+  *total = tot;
+  return off + incl;
+}
+
+template <typename E, int D>
+__device__ __forceinline__ void write_empty_unit(E* out, float* lse, int u, int Hkv, int G) {
+  const int b = u / Hkv, h = u % Hkv;
+  for (int gg = 0; gg < G; ++gg) {
+    const size_t orow = (size_t)b * Hkv * G + (size_t)h * G + gg;
+    for (int c = 0; c < D; ++c) store_elem(out + orow * D + c, 0.0f);
+    if (lse) lse[orow] = -__builtin_inff();
+  }
+}
 
 template <typename E, int D, int G, int U>
 __global__ __launch_bounds__(NT) void k_decode(
@@ -164,386 +203,455 @@ __global__ __launch_bounds__(NT) void k_decode(
     const E* __restrict__ V, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ sel_cnt, float scale_log2,
     E* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
-    float2* __restrict__ part_ml, uint32_t* __restrict__ err, int Hkv, int t_cap, int max_sel,
-    int split, int log2split, int max_chunks) {
+    float2* __restrict__ part_ml, int2* __restrict__ seg_rec, uint32_t* __restrict__ err,
+    int Hkv, int t_cap, int max_sel, int n_units, int split) {
   constexpr int EPL = Lanes<E>::EPL;
   constexpr int LPT = D / EPL;        // lanes per token
   constexpr int TPW = 64 / LPT;       // tokens per wave instruction
   constexpr int STEP = TPW * U;       // tokens per wave per step
   static_assert(LPT >= 4 && LPT <= 32 && 64 % LPT == 0, "lane layout");
   __shared__ DecodeLds<E, D, G> L;
+  const int P = gridDim.x, seg = blockIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
 
-  const int stride = max_chunks | 1;
-  const int u = blockIdx.x / stride;
-  const int chunk = blockIdx.x % stride;
-  const UnitInfo ui = units[u];
-  const int b = u / Hkv, h = u % Hkv;
-  const int32_t* sel = sel_idx + (size_t)u * max_sel;
-  const UnitSpan sp = unit_span(ui, seq_lens, sel, sel_cnt, u, b, t_cap, max_sel, split,
-                                log2split, max_chunks, err);
-  if (chunk >= sp.nchunks) return;
-  const int T = sp.T, g = ui.g, log2g = ui.log2g;
+  // ---- Scan 1: every unit's token count and the total (errors reported here only).
+  int keepN[kScanKeep];
+  int mysum = 0;
+  for (int c0 = 0; c0 < n_units; c0 += kScanKeep * NT) {
+    int Nk[kScanKeep];
+#pragma unroll
+    for (int k = 0; k < kScanKeep; ++k) {
+      const int u = c0 + k * NT + (int)threadIdx.x;
+      Nk[k] = u < n_units ? unit_tokens(units, seq_lens, sel_idx, sel_cnt, u, Hkv, t_cap, max_sel,
+                                        seg == 0, err).N
+                          : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < kScanKeep; ++k) {
+      if (c0 == 0) keepN[k] = Nk[k];
+      mysum += Nk[k];
+    }
+  }
+  int total = (int)wave_sum_u32((uint32_t)mysum);
+  if (lane == 0) L.scan[0][wave] = total;
+  __syncthreads();
+  total = 0;
+#pragma unroll
+  for (int i = 0; i < NWAVES; ++i) total += L.scan[0][i];
+  total = __builtin_amdgcn_readfirstlane(total);   // uniform: keep what follows scalar
+  const int S = max((total + P - 1) / P, split);
+  const int nseg = (total + S - 1) / S;
+  const int s0 = seg * S, s1 = min(s0 + S, total);
 
-  const int i0 = chunk * sp.clen;
-  const int i1 = min(sp.N, i0 + sp.clen);
-  // Block indices this chunk touches; entries that are not valid blocks of the unit, in
-  // ascending order, become -1 (their tokens are skipped).
-  const int p0 = i0 >> log2g;
-  const int np = i1 > i0 ? ((i1 - 1) >> log2g) - p0 + 1 : 0;
-  for (int i = threadIdx.x; i < np; i += NT) {
-    const int jb = sel[p0 + i];
-    const bool ok = jb >= 0 && (int64_t)jb * g < T && (p0 + i == 0 || sel[p0 + i - 1] < jb);
-    if (!ok) atomicOr(err, (uint32_t)FX_ERR_SEL_INDEX);
-    L.blk[i] = ok ? jb : -1;
+  // ---- Scan 2: prefix sums; the unit holding token s0; units without tokens.
+  int running = 0, it = 0;
+  for (int c0 = 0; c0 < n_units; c0 += NT, ++it) {
+    const int u = c0 + (int)threadIdx.x;
+    int N = 0;
+    if (c0 < kScanKeep * NT) {
+#pragma unroll
+      for (int k = 0; k < kScanKeep; ++k) N = (c0 == k * NT) ? keepN[k] : N;
+    } else if (u < n_units) {
+      N = unit_tokens(units, seq_lens, sel_idx, sel_cnt, u, Hkv, t_cap, max_sel, false, err).N;
+    }
+    int chunk_total;
+    const int incl = running + block_incl_scan(N, L.scan[(it + 1) & 1], &chunk_total);
+    const int excl = incl - N;
+    if (N > 0 && excl <= s0 && s0 < incl) {
+      L.first_unit = u;
+      L.first_pos = excl;
+    }
+    if (u < n_units && N == 0 && u % P == seg) write_empty_unit<E, D>(out, lse, u, Hkv, G);
+    running += chunk_total;
+  }
+  if (seg >= nseg) {
+    if (threadIdx.x == 0) seg_rec[seg] = make_int2(-1, 0);
+    return;
   }
   __syncthreads();
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t lane_off = (uint32_t)(lane % LPT) * 16u;
   const int lg = lane / LPT, li = lane % LPT;
-
-  // Query slices: this lane's 16 bytes of each of the G rows.
-  const size_t unit_rows = (size_t)u * t_cap;
-  const E* qrow = q + ((size_t)b * Hkv * G + (size_t)h * G) * D + li * EPL;
-  uint4 qv[G];
-#pragma unroll
-  for (int gg = 0; gg < G; ++gg) qv[gg] = *reinterpret_cast<const uint4*>(qrow + (size_t)gg * D);
-
-  float m[G], l[G], o[G][EPL == 8 ? 8 : EPL];
-#pragma unroll
-  for (int gg = 0; gg < G; ++gg) {
-    m[gg] = kNegBig;
-    l[gg] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) o[gg][e] = 0.0f;
-  }
-
-  // This wave's share of the chunk (a multiple of STEP tokens).
-  const int per_wave = ((sp.clen + NWAVES * STEP - 1) / (NWAVES * STEP)) * STEP;
-  const int w0 = i0 + wave * per_wave;
-  const int w1 = min(i1, w0 + per_wave);
-  // The unit's rows [0, T) of K and V as buffer resources: rows past T, and masked
-  // token slots (sent to kOutOfRange), read as zeros with no memory access.
   constexpr uint32_t kRowBytes = D * sizeof(E);
-  const uint32_t nbytes = (uint32_t)T * kRowBytes;
-  const __amdgpu_buffer_rsrc_t rk =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(K + unit_rows * D), 0, (int)nbytes, kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rv =
-      __builtin_amdgcn_make_buffer_rsrc((void*)(V + unit_rows * D), 0, (int)nbytes, kRsrcWord3);
-  const uint32_t lane_off = (uint32_t)li * 16u;
-
-  auto load_step = [&](int base, uint4* kr, uint4* vr, bool* ok) {
-    // Block indices first (independent LDS reads), then all 2U buffer loads.
-    int jb[U];
-#pragma unroll
-    for (int uu = 0; uu < U; ++uu) {
-      const int i = base + uu * TPW + lg;
-      jb[uu] = L.blk[max(0, min((i >> log2g) - p0, np - 1))];
+  bool recorded = false;
+  int u = __builtin_amdgcn_readfirstlane(L.first_unit);
+  int Pu = __builtin_amdgcn_readfirstlane(L.first_pos);
+  int cur = s0;
+  while (cur < s1) {
+    const UnitTokens ut =
+        unit_tokens(units, seq_lens, sel_idx, sel_cnt, u, Hkv, t_cap, max_sel, false, err);
+    const int N = ut.N;
+    if (N == 0) {
+      ++u;
+      continue;
     }
-#pragma unroll
-    for (int uu = 0; uu < U; ++uu) {
-      const int i = base + uu * TPW + lg;
-      const int row = jb[uu] * g + (i & (g - 1));
-      ok[uu] = i < w1 && jb[uu] >= 0 && row < T;
-      const uint32_t off = ok[uu] ? (uint32_t)row * kRowBytes + lane_off : kOutOfRange;
-      kr[uu] = buffer_load16(rk, off);
-      vr[uu] = buffer_load16(rv, off);
-    }
-  };
+    const int T = ut.T;
+    const UnitInfo ui = units[u];
+    const int g = ui.g, log2g = ui.log2g;
+    const int b = u / Hkv, h = u % Hkv;
+    const int32_t* sel = sel_idx + (size_t)u * max_sel;
+    const int a = cur - Pu, e = min(s1, Pu + N) - Pu;   // piece [a, e) of the unit's tokens
 
-  auto compute_step = [&](const uint4* kr, const uint4* vr, const bool* ok) {
-    float s[U][G];
+    // Query slices: this lane's 16 bytes of each of the G rows.
+    const E* qrow = q + ((size_t)b * Hkv * G + (size_t)h * G) * D + li * EPL;
+    uint4 qv[G];
 #pragma unroll
-    for (int uu = 0; uu < U; ++uu)
-#pragma unroll
-      for (int gg = 0; gg < G; ++gg) s[uu][gg] = lane_dot(qv[gg], kr[uu], (E*)nullptr);
-#pragma unroll
-    for (int uu = 0; uu < U; ++uu)
-#pragma unroll
-      for (int gg = 0; gg < G; ++gg) {
-        const float t = group_sum<LPT>(s[uu][gg]) * scale_log2;
-        s[uu][gg] = ok[uu] ? t : -__builtin_inff();
-      }
-    // Rescale o and l only when some running max of the wave grew (a wave-uniform
-    // branch); otherwise every alpha would be exactly 1.
-    float mx[G];
-    bool grow = false;
+    for (int gg = 0; gg < G; ++gg) qv[gg] = *reinterpret_cast<const uint4*>(qrow + (size_t)gg * D);
+    float m[G], l[G], o[G][EPL == 8 ? 8 : EPL];
 #pragma unroll
     for (int gg = 0; gg < G; ++gg) {
-      mx[gg] = m[gg];
+      m[gg] = kNegBig;
+      l[gg] = 0.0f;
 #pragma unroll
-      for (int uu = 0; uu < U; ++uu) mx[gg] = fmaxf(mx[gg], s[uu][gg]);
-      grow |= mx[gg] > m[gg];
+      for (int x = 0; x < EPL; ++x) o[gg][x] = 0.0f;
     }
-    if (__builtin_expect(__builtin_amdgcn_ballot_w64(grow) != 0, 0)) {
-      // Keep this a branch: if-converting it would run the rescale every step.
-      asm volatile("" ::: "memory");
+    // The unit's rows [0, T) of K and V as buffer resources: rows past T, and masked
+    // token slots (sent to kOutOfRange), read as zeros with no memory access.
+    const size_t unit_rows = (size_t)u * t_cap;
+    const uint32_t nbytes = (uint32_t)T * kRowBytes;
+    const __amdgpu_buffer_rsrc_t rk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(K + unit_rows * D), 0, (int)nbytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(V + unit_rows * D), 0, (int)nbytes, kRsrcWord3);
+
+    for (int c0 = a; c0 < e; c0 += kMaxSplit) {
+      const int c1 = min(e, c0 + kMaxSplit);
+      // Block indices this run touches; entries that are not valid blocks of the unit,
+      // in ascending order, become -1 (their tokens are skipped).
+      const int p0 = c0 >> log2g;
+      const int np = ((c1 - 1) >> log2g) - p0 + 1;
+      __syncthreads();   // the previous run's readers of L.blk are done
+      for (int i = threadIdx.x; i < np; i += NT) {
+        const int jb = sel[p0 + i];
+        const bool ok = jb >= 0 && (int64_t)jb * g < T && (p0 + i == 0 || sel[p0 + i - 1] < jb);
+        if (!ok) atomicOr(err, (uint32_t)FX_ERR_SEL_INDEX);
+        L.blk[i] = ok ? jb : -1;
+      }
+      __syncthreads();
+
+      // This wave's share of the run (a multiple of STEP tokens).
+      const int per_wave = ((c1 - c0 + NWAVES * STEP - 1) / (NWAVES * STEP)) * STEP;
+      const int w0 = c0 + wave * per_wave;
+      const int w1 = min(c1, w0 + per_wave);
+
+      auto load_step = [&](int base, uint4* kr, uint4* vr, bool* ok) {
+        // Block indices first (independent LDS reads), then all 2U buffer loads.
+        int jb[U];
+#pragma unroll
+        for (int uu = 0; uu < U; ++uu) {
+          const int i = base + uu * TPW + lg;
+          jb[uu] = L.blk[max(0, min((i >> log2g) - p0, np - 1))];
+        }
+#pragma unroll
+        for (int uu = 0; uu < U; ++uu) {
+          const int i = base + uu * TPW + lg;
+          const int row = jb[uu] * g + (i & (g - 1));
+          ok[uu] = i < w1 && jb[uu] >= 0 && row < T;
+          const uint32_t off = ok[uu] ? (uint32_t)row * kRowBytes + lane_off : kOutOfRange;
+          kr[uu] = buffer_load16(rk, off);
+          vr[uu] = buffer_load16(rv, off);
+        }
+      };
+
+      auto compute_step = [&](const uint4* kr, const uint4* vr, const bool* ok) {
+        float sc[U][G];
+#pragma unroll
+        for (int uu = 0; uu < U; ++uu)
+#pragma unroll
+          for (int gg = 0; gg < G; ++gg) sc[uu][gg] = lane_dot(qv[gg], kr[uu], (E*)nullptr);
+#pragma unroll
+        for (int uu = 0; uu < U; ++uu)
+#pragma unroll
+          for (int gg = 0; gg < G; ++gg) {
+            const float t = group_sum<LPT>(sc[uu][gg]) * scale_log2;
+            sc[uu][gg] = ok[uu] ? t : -__builtin_inff();
+          }
+        // Rescale o and l only when some running max of the wave grew (a wave-uniform
+        // branch); otherwise every alpha would be exactly 1.
+        float mx[G];
+        bool grow = false;
+#pragma unroll
+        for (int gg = 0; gg < G; ++gg) {
+          mx[gg] = m[gg];
+#pragma unroll
+          for (int uu = 0; uu < U; ++uu) mx[gg] = fmaxf(mx[gg], sc[uu][gg]);
+          grow |= mx[gg] > m[gg];
+        }
+        if (__builtin_expect(__builtin_amdgcn_ballot_w64(grow) != 0, 0)) {
+          // Keep this a branch: if-converting it would run the rescale every step.
+          asm volatile("" ::: "memory");
+#pragma unroll
+          for (int gg = 0; gg < G; ++gg) {
+            const float alpha = __builtin_amdgcn_exp2f(m[gg] - mx[gg]);
+            m[gg] = mx[gg];
+            l[gg] *= alpha;
+#pragma unroll
+            for (int x = 0; x < EPL; ++x) o[gg][x] *= alpha;
+          }
+        }
+        float pr[U][G];
+#pragma unroll
+        for (int uu = 0; uu < U; ++uu)
+#pragma unroll
+          for (int gg = 0; gg < G; ++gg) {
+            pr[uu][gg] = __builtin_amdgcn_exp2f(sc[uu][gg] - m[gg]);
+            l[gg] += pr[uu][gg];
+          }
+        if constexpr (sizeof(E) == 2) {
+          static_assert(U % 2 == 0, "token pairs");
+#pragma unroll
+          for (int uu = 0; uu < U; uu += 2) pv_pair<G>(pr[uu], pr[uu + 1], vr[uu], vr[uu + 1], o);
+        } else {
+#pragma unroll
+          for (int uu = 0; uu < U; ++uu) {
+            float vf[EPL];
+            unpack(vr[uu], vf, (E*)nullptr);
+#pragma unroll
+            for (int gg = 0; gg < G; ++gg)
+#pragma unroll
+              for (int x = 0; x < EPL; ++x) o[gg][x] = fmaf(pr[uu][gg], vf[x], o[gg][x]);
+          }
+        }
+      };
+
+      // Register double buffering: the loads of step n+1 are in flight while step n
+      // computes.  The loads are issued unconditionally (slots past w1 are out of range
+      // and cost no memory traffic) so the count of outstanding loads is the same on
+      // every path and each compute waits only for its own step's loads.
+      uint4 kA[U], vA[U], kB[U], vB[U];
+      bool okA[U], okB[U];
+      if (w0 < w1) {
+        load_step(w0, kA, vA, okA);
+        for (int base = w0; base < w1; base += 2 * STEP) {
+          load_step(base + STEP, kB, vB, okB);
+          compute_step(kA, vA, okA);
+          load_step(base + 2 * STEP, kA, vA, okA);
+          if (base + STEP < w1) compute_step(kB, vB, okB);
+        }
+      }
+    }
+
+    // Merge the lane groups of the wave (partners differ in the lane bits above LPT).
+#pragma unroll
+    for (int off = LPT; off < 64; off <<= 1) {
 #pragma unroll
       for (int gg = 0; gg < G; ++gg) {
-        const float alpha = __builtin_amdgcn_exp2f(m[gg] - mx[gg]);
-        m[gg] = mx[gg];
-        l[gg] *= alpha;
+        const float m2 = __shfl_xor(m[gg], off);
+        const float l2 = __shfl_xor(l[gg], off);
+        const float M = fmaxf(m[gg], m2);
+        const float x = __builtin_amdgcn_exp2f(m[gg] - M);
+        const float y = __builtin_amdgcn_exp2f(m2 - M);
+        l[gg] = l[gg] * x + l2 * y;
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) o[gg][e] *= alpha;
+        for (int z = 0; z < EPL; ++z) {
+          const float o2 = __shfl_xor(o[gg][z], off);
+          o[gg][z] = o[gg][z] * x + o2 * y;
+        }
+        m[gg] = M;
       }
     }
-    float p[U][G];
-#pragma unroll
-    for (int uu = 0; uu < U; ++uu)
+    if (lg == 0) {
 #pragma unroll
       for (int gg = 0; gg < G; ++gg) {
-        p[uu][gg] = __builtin_amdgcn_exp2f(s[uu][gg] - m[gg]);
-        l[gg] += p[uu][gg];
-      }
-    if constexpr (sizeof(E) == 2) {
-      static_assert(U % 2 == 0, "token pairs");
 #pragma unroll
-      for (int uu = 0; uu < U; uu += 2) pv_pair<G>(p[uu], p[uu + 1], vr[uu], vr[uu + 1], o);
-    } else {
-#pragma unroll
-      for (int uu = 0; uu < U; ++uu) {
-        float vf[EPL];
-        unpack(vr[uu], vf, (E*)nullptr);
-#pragma unroll
-        for (int gg = 0; gg < G; ++gg)
-#pragma unroll
-          for (int e = 0; e < EPL; ++e) o[gg][e] = fmaf(p[uu][gg], vf[e], o[gg][e]);
+        for (int z = 0; z < EPL; ++z) L.o[wave][gg][li * EPL + z] = o[gg][z];
+        if (li == 0) {
+          L.m[wave][gg] = m[gg];
+          L.l[wave][gg] = l[gg];
+        }
       }
     }
-  };
+    __syncthreads();
 
-  // Register double buffering: the loads of step n+1 are in flight while step n
-  // computes.  The loads are issued unconditionally (slots past w1 are out of range and
-  // cost no memory traffic) so the count of outstanding loads is the same on every path
-  // and each compute waits only for its own step's loads.
-  uint4 kA[U], vA[U], kB[U], vB[U];
-  bool okA[U], okB[U];
-  if (w0 < w1) {
-    load_step(w0, kA, vA, okA);
-    for (int base = w0; base < w1; base += 2 * STEP) {
-      load_step(base + STEP, kB, vB, okB);
-      compute_step(kA, vA, okA);
-      load_step(base + 2 * STEP, kA, vA, okA);
-      if (base + STEP < w1) compute_step(kB, vB, okB);
-    }
-  }
-
-  // Merge the lane groups of the wave (partners differ in the lane bits above LPT).
+    // Merge the waves in wave order; then finish the unit or publish a partial.
+    const bool whole = a == 0 && e == N;
+    const size_t pbase = (size_t)seg * 2 + (a == 0 ? 1 : 0);
+    for (int idx = threadIdx.x; idx < G * D; idx += NT) {
+      const int gg = idx / D, c = idx % D;
+      float M = L.m[0][gg];
 #pragma unroll
-  for (int off = LPT; off < 64; off <<= 1) {
+      for (int w = 1; w < NWAVES; ++w) M = fmaxf(M, L.m[w][gg]);
+      float Ls = 0.0f, Os = 0.0f;
 #pragma unroll
-    for (int gg = 0; gg < G; ++gg) {
-      const float m2 = __shfl_xor(m[gg], off);
-      const float l2 = __shfl_xor(l[gg], off);
-      const float M = fmaxf(m[gg], m2);
-      const float a = __builtin_amdgcn_exp2f(m[gg] - M);
-      const float c = __builtin_amdgcn_exp2f(m2 - M);
-      l[gg] = l[gg] * a + l2 * c;
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) {
-        const float o2 = __shfl_xor(o[gg][e], off);
-        o[gg][e] = o[gg][e] * a + o2 * c;
+      for (int w = 0; w < NWAVES; ++w) {
+        const float x = __builtin_amdgcn_exp2f(L.m[w][gg] - M);
+        Ls = fmaf(L.l[w][gg], x, Ls);
+        Os = fmaf(L.o[w][gg][c], x, Os);
       }
-      m[gg] = M;
-    }
-  }
-  if (lg == 0) {
-#pragma unroll
-    for (int gg = 0; gg < G; ++gg) {
-#pragma unroll
-      for (int e = 0; e < EPL; ++e) L.o[wave][gg][li * EPL + e] = o[gg][e];
-      if (li == 0) {
-        L.m[wave][gg] = m[gg];
-        L.l[wave][gg] = l[gg];
+      if (whole) {
+        const size_t orow = (size_t)b * Hkv * G + (size_t)h * G + gg;
+        store_elem(out + orow * D + c, Ls > 0.0f ? Os / Ls : 0.0f);
+        if (lse && c == 0) lse[orow] = Ls > 0.0f ? (M + __log2f(Ls)) * kLn2 : -__builtin_inff();
+      } else {
+        part_o[(pbase * G + gg) * D + c] = Os;
+        if (c == 0) part_ml[pbase * G + gg] = make_float2(M, Ls);
       }
     }
-  }
-  __syncthreads();
-
-  // Merge the waves in wave order; then either finish the unit or publish a partial.
-  const bool single = sp.nchunks == 1;
-  const size_t pbase = (size_t)u * max_chunks + chunk;
-  for (int idx = threadIdx.x; idx < G * D; idx += NT) {
-    const int gg = idx / D, c = idx % D;
-    float M = L.m[0][gg];
-#pragma unroll
-    for (int w = 1; w < NWAVES; ++w) M = fmaxf(M, L.m[w][gg]);
-    float Ls = 0.0f, Os = 0.0f;
-#pragma unroll
-    for (int w = 0; w < NWAVES; ++w) {
-      const float a = __builtin_amdgcn_exp2f(L.m[w][gg] - M);
-      Ls = fmaf(L.l[w][gg], a, Ls);
-      Os = fmaf(L.o[w][gg][c], a, Os);
+    if (a == 0 && e < N) {
+      // The unit continues in the following segments: its pieces are this segment's
+      // tail slot and the head slots of segments seg+1 .. seg+n-1.
+      if (threadIdx.x == 0) seg_rec[seg] = make_int2(u, (Pu + N - 1) / S - seg + 1);
+      recorded = true;
     }
-    if (single) {
-      const size_t orow = (size_t)b * Hkv * G + (size_t)h * G + gg;
-      store_elem(out + orow * D + c, Ls > 0.0f ? Os / Ls : 0.0f);
-      if (lse && c == 0) lse[orow] = Ls > 0.0f ? (M + __log2f(Ls)) * kLn2 : -__builtin_inff();
-    } else {
-      part_o[(pbase * G + gg) * D + c] = Os;
-      if (c == 0) part_ml[pbase * G + gg] = make_float2(M, Ls);
-    }
+    cur = Pu + e;
+    Pu += N;
+    ++u;
   }
+  if (!recorded && threadIdx.x == 0) seg_rec[seg] = make_int2(-1, 0);
 }
 
-// Reductions over the 256 threads of a workgroup (lds: NWAVES floats).
-__device__ __forceinline__ float block_max(float x, float* lds) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x = fmaxf(x, __shfl_xor(x, off));
-  if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = x;
-  __syncthreads();
-  float r = lds[0];
-#pragma unroll
-  for (int w = 1; w < NWAVES; ++w) r = fmaxf(r, lds[w]);
-  __syncthreads();
-  return r;
-}
-__device__ __forceinline__ float block_sum_f(float x, float* lds) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off);
-  if ((threadIdx.x & 63) == 0) lds[threadIdx.x >> 6] = x;
-  __syncthreads();
-  float r = 0.0f;
-#pragma unroll
-  for (int w = 0; w < NWAVES; ++w) r += lds[w];   // fixed order: deterministic
-  __syncthreads();
-  return r;
+// Partial slot of piece k of the unit recorded by segment s.
+__device__ __forceinline__ size_t piece_slot(int s, int k) {
+  return k == 0 ? (size_t)s * 2 + 1 : (size_t)(s + k) * 2;
 }
 
-constexpr int kCombineTile = 256;   // chunks whose weights sit in LDS at a time
+// One workgroup per segment with one thread per output (query row, column); each thread
+// merges its own pieces in piece order, eight at a time (all sixteen loads in flight), with a
+// running max: M = max m_k, L = sum l_k 2^(m_k - M), out = sum o_k 2^(m_k - M) / L.
+// No LDS and no barriers; the (m, l) loads repeat across a row's threads and hit the
+// cache.
+constexpr int kMergeBatch = 8;
 
 template <typename E, int D, int G>
-__global__ __launch_bounds__(NT) void k_combine(
-    const UnitInfo* __restrict__ units, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ sel_cnt,
-    E* __restrict__ out, float* __restrict__ lse, const float* __restrict__ part_o,
-    const float2* __restrict__ part_ml, uint32_t* __restrict__ err, int Hkv, int t_cap,
-    int max_sel, int split, int log2split, int max_chunks) {
-  constexpr int OUTS = (G * D + NT - 1) / NT;   // outputs per thread
-  __shared__ float red[NWAVES];
-  __shared__ float Mg[G], Lg[G];
-  __shared__ float wts[kCombineTile][G];
-  const int u = blockIdx.x;
-  const UnitInfo ui = units[u];
+__global__ __launch_bounds__(1024) void k_combine(
+    const int2* __restrict__ seg_rec, E* __restrict__ out, float* __restrict__ lse,
+    const float* __restrict__ part_o, const float2* __restrict__ part_ml, int Hkv) {
+  const int s = blockIdx.x;
+  const int2 rec = seg_rec[s];
+  if (rec.x < 0) return;
+  const int u = rec.x, nk = min(rec.y, (int)gridDim.x - s);
   const int b = u / Hkv, h = u % Hkv;
-  const UnitSpan sp = unit_span(ui, seq_lens, sel_idx + (size_t)u * max_sel, sel_cnt, u, b,
-                                t_cap, max_sel, split, log2split, max_chunks, err);
-  if (sp.nchunks == 1) return;   // k_decode already wrote this unit
-  const int nk = sp.nchunks;
-  const float2* ml = part_ml + (size_t)u * max_chunks * G;
-  const float* po = part_o + (size_t)u * max_chunks * G * D;
-
-  // Per query row: M = max over chunks of m, L = sum over chunks of l * 2^(m - M).
-  for (int gg = 0; gg < G; ++gg) {
-    float mx = kNegBig;
-    for (int k = threadIdx.x; k < nk; k += NT) mx = fmaxf(mx, ml[(size_t)k * G + gg].x);
-    const float M = block_max(mx, red);
-    float ls = 0.0f;
-    for (int k = threadIdx.x; k < nk; k += NT) {
-      const float2 v = ml[(size_t)k * G + gg];
-      ls += v.y * __builtin_amdgcn_exp2f(v.x - M);
-    }
-    const float L = block_sum_f(ls, red);
-    if (threadIdx.x == 0) {
-      Mg[gg] = M;
-      Lg[gg] = L;
-    }
-  }
-  __syncthreads();
-
-  // out = sum over chunks of o_k * 2^(m_k - M) / L, chunks taken in order.
-  float acc[OUTS];
+  for (int idx = threadIdx.x; idx < G * D; idx += blockDim.x) {
+    const int gg = idx / D, c = idx % D;
+    float M = kNegBig, Lt = 0.0f, acc = 0.0f;
+    for (int k0 = 0; k0 < nk; k0 += kMergeBatch) {
+      float2 ml[kMergeBatch];
+      float ov[kMergeBatch];
 #pragma unroll
-  for (int j = 0; j < OUTS; ++j) acc[j] = 0.0f;
-  for (int k0 = 0; k0 < nk; k0 += kCombineTile) {
-    const int kt = min(kCombineTile, nk - k0);
-    for (int i = threadIdx.x; i < kt * G; i += NT) {
-      const int k = i / G, gg = i % G;
-      wts[k][gg] = __builtin_amdgcn_exp2f(ml[(size_t)(k0 + k) * G + gg].x - Mg[gg]);
-    }
-    __syncthreads();
+      for (int j = 0; j < kMergeBatch; ++j) {
+        const int k = k0 + j;
+        if (k < nk) {
+          const size_t slot = piece_slot(s, k);
+          ml[j] = part_ml[slot * G + gg];
+          ov[j] = part_o[slot * G * D + idx];
+        } else {
+          ml[j] = make_float2(kNegBig, 0.0f);
+          ov[j] = 0.0f;
+        }
+      }
+      float Mn = M;
 #pragma unroll
-    for (int j = 0; j < OUTS; ++j) {
-      const int idx = threadIdx.x + j * NT;
-      if (idx < G * D) {
-        const int gg = idx / D;
-        const float* src = po + (size_t)k0 * G * D + idx;
-        float a = acc[j];
-#pragma unroll 8
-        for (int k = 0; k < kt; ++k) a = fmaf(src[(size_t)k * G * D], wts[k][gg], a);
-        acc[j] = a;
+      for (int j = 0; j < kMergeBatch; ++j) Mn = fmaxf(Mn, ml[j].x);
+      const float r = __builtin_amdgcn_exp2f(M - Mn);
+      Lt *= r;
+      acc *= r;
+      M = Mn;
+#pragma unroll
+      for (int j = 0; j < kMergeBatch; ++j) {
+        const float wgt = __builtin_amdgcn_exp2f(ml[j].x - M);
+        Lt = fmaf(ml[j].y, wgt, Lt);
+        acc = fmaf(ov[j], wgt, acc);
       }
     }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int j = 0; j < OUTS; ++j) {
-    const int idx = threadIdx.x + j * NT;
-    if (idx < G * D) {
-      const int gg = idx / D, c = idx % D;
-      const float L = Lg[gg];
-      const size_t orow = (size_t)b * Hkv * G + (size_t)h * G + gg;
-      store_elem(out + orow * D + c, L > 0.0f ? acc[j] / L : 0.0f);
-      if (lse && c == 0) lse[orow] = L > 0.0f ? (Mg[gg] + __log2f(L)) * kLn2 : -__builtin_inff();
-    }
+    const size_t orow = (size_t)b * Hkv * G + (size_t)h * G + gg;
+    store_elem(out + orow * D + c, Lt > 0.0f ? acc / Lt : 0.0f);
+    if (lse && c == 0) lse[orow] = Lt > 0.0f ? (M + __log2f(Lt)) * kLn2 : -__builtin_inff();
   }
 }
+
+constexpr int kU = 4;   // tokens per lane group per step
 
 template <typename E, int D, int G>
 hipError_t launch_t(const fx_plan* p, const void* q, const void* K, const void* V,
                     const int32_t* seq_lens, const int32_t* sel_idx, const int32_t* sel_cnt,
                     float softmax_scale, void* out, float* lse, float* part_o, float* part_ml,
-                    hipStream_t stream) {
-  constexpr int U = 4;
+                    int2* seg_rec, hipStream_t stream) {
   const int Hkv = p->desc.num_kv_heads, t_cap = p->desc.t_cap;
-  const dim3 grid((unsigned)((int64_t)p->units * (p->max_chunks | 1)));
-  k_decode<E, D, G, U><<<grid, NT, 0, stream>>>(
+  const dim3 grid((unsigned)p->decode_grid);
+  k_decode<E, D, G, kU><<<grid, NT, 0, stream>>>(
       p->d_units, static_cast<const E*>(q), static_cast<const E*>(K), static_cast<const E*>(V),
       seq_lens, sel_idx, sel_cnt, softmax_scale * kLog2e, static_cast<E*>(out), lse, part_o,
-      reinterpret_cast<float2*>(part_ml), p->d_error, Hkv, t_cap, p->max_sel, p->split,
-      p->log2split, p->max_chunks);
+      reinterpret_cast<float2*>(part_ml), seg_rec, p->d_error, Hkv, t_cap, p->max_sel, p->units,
+      p->split);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p->max_chunks == 1) return e;
-  k_combine<E, D, G><<<dim3((unsigned)p->units), NT, 0, stream>>>(
-      p->d_units, seq_lens, sel_idx, sel_cnt, static_cast<E*>(out), lse, part_o,
-      reinterpret_cast<const float2*>(part_ml), p->d_error, Hkv, t_cap, p->max_sel, p->split,
-      p->log2split, p->max_chunks);
+  if (e != hipSuccess) return e;
+  // One thread per output (query row, column).
+  constexpr int kCombineThreads = G * D < 1024 ? G * D : 1024;
+  k_combine<E, D, G><<<grid, kCombineThreads, 0, stream>>>(
+      seg_rec, static_cast<E*>(out), lse, part_o, reinterpret_cast<const float2*>(part_ml), Hkv);
   return hipGetLastError();
 }
 
-template <typename E, int D>
-hipError_t dispatch_g(const fx_plan* p, const void* q, const void* K, const void* V,
-                      const int32_t* seq_lens, const int32_t* sel_idx, const int32_t* sel_cnt,
-                      float scale, void* out, float* lse, float* po, float* pml,
-                      hipStream_t s) {
-  switch (p->G) {
-    case 1: return launch_t<E, D, 1>(p, q, K, V, seq_lens, sel_idx, sel_cnt, scale, out, lse, po, pml, s);
-    case 2: return launch_t<E, D, 2>(p, q, K, V, seq_lens, sel_idx, sel_cnt, scale, out, lse, po, pml, s);
-    case 3: return launch_t<E, D, 3>(p, q, K, V, seq_lens, sel_idx, sel_cnt, scale, out, lse, po, pml, s);
-    case 4: return launch_t<E, D, 4>(p, q, K, V, seq_lens, sel_idx, sel_cnt, scale, out, lse, po, pml, s);
-    case 5: return launch_t<E, D, 5>(p, q, K, V, seq_lens, sel_idx, sel_cnt, scale, out, lse, po, pml, s);
-    case 6: return launch_t<E, D, 6>(p, q, K, V, seq_lens, sel_idx, sel_cnt, scale, out, lse, po, pml, s);
-    case 7: return launch_t<E, D, 7>(p, q, K, V, seq_lens, sel_idx, sel_cnt, scale, out, lse, po, pml, s);
-    case 8: return launch_t<E, D, 8>(p, q, K, V, seq_lens, sel_idx, sel_cnt, scale, out, lse, po, pml, s);
-  }
-  return hipErrorInvalidValue;
+template <typename E, int D, int G>
+int grid_t() {
+  int per_cu = 0, cus = 0, dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &per_cu, reinterpret_cast<const void*>(&k_decode<E, D, G, kU>), NT, 0) != hipSuccess)
+    return 0;
+  return per_cu * cus;
 }
 
+// Calls f.template operator()<E, D, G>() for the plan's element type, head dim and group.
+template <typename F>
+auto with_shape(const fx_plan* p, F&& f) {
+  auto by_g = [&](auto e_tag, auto d_tag) {
+    using E = typename decltype(e_tag)::type;
+    constexpr int D = decltype(d_tag)::value;
+    switch (p->G) {
+      case 1: return f.template operator()<E, D, 1>();
+      case 2: return f.template operator()<E, D, 2>();
+      case 3: return f.template operator()<E, D, 3>();
+      case 4: return f.template operator()<E, D, 4>();
+      case 5: return f.template operator()<E, D, 5>();
+      case 6: return f.template operator()<E, D, 6>();
+      case 7: return f.template operator()<E, D, 7>();
+      default: return f.template operator()<E, D, 8>();
+    }
+  };
+  struct Bf { using type = bf16_t; };
+  struct Fl { using type = float; };
+  if (p->desc.dtype == FX_BF16)
+    return p->desc.head_dim == 128 ? by_g(Bf{}, std::integral_constant<int, 128>{})
+                                   : by_g(Bf{}, std::integral_constant<int, 64>{});
+  return p->desc.head_dim == 128 ? by_g(Fl{}, std::integral_constant<int, 128>{})
+                                 : by_g(Fl{}, std::integral_constant<int, 64>{});
+}
+
+struct GridFn {
+  template <typename E, int D, int G>
+  int operator()() const { return grid_t<E, D, G>(); }
+};
+
+struct LaunchFn {
+  const fx_plan* p;
+  const void *q, *K, *V;
+  const int32_t *seq_lens, *sel_idx, *sel_cnt;
+  float softmax_scale;
+  void* out;
+  float *lse, *part_o, *part_ml;
+  int2* seg_rec;
+  hipStream_t stream;
+  template <typename E, int D, int G>
+  hipError_t operator()() const {
+    return launch_t<E, D, G>(p, q, K, V, seq_lens, sel_idx, sel_cnt, softmax_scale, out, lse,
+                             part_o, part_ml, seg_rec, stream);
+  }
+};
+
 }  // namespace
+
+int decode_grid(const fx_plan* p) { return with_shape(p, GridFn{}); }
 
 hipError_t launch_decode(const fx_plan* p, const void* q, const void* K, const void* V,
                          const int32_t* seq_lens, const int32_t* sel_idx, const int32_t* sel_cnt,
                          float softmax_scale, void* out, float* lse, float* part_o,
-                         float* part_ml, hipStream_t stream) {
-  const int d = p->desc.head_dim;
-  if (p->desc.dtype == FX_BF16)
-    return d == 128 ? dispatch_g<bf16_t, 128>(p, q, K, V, seq_lens, sel_idx, sel_cnt,
-                                              softmax_scale, out, lse, part_o, part_ml, stream)
-                    : dispatch_g<bf16_t, 64>(p, q, K, V, seq_lens, sel_idx, sel_cnt,
-                                             softmax_scale, out, lse, part_o, part_ml, stream);
-  return d == 128 ? dispatch_g<float, 128>(p, q, K, V, seq_lens, sel_idx, sel_cnt, softmax_scale,
-                                           out, lse, part_o, part_ml, stream)
-                  : dispatch_g<float, 64>(p, q, K, V, seq_lens, sel_idx, sel_cnt, softmax_scale,
-                                          out, lse, part_o, part_ml, stream);
+                         float* part_ml, int32_t* seg_rec, hipStream_t stream) {
+  if (p->G < 1 || p->G > kMaxGroup) return hipErrorInvalidValue;
+  return with_shape(p, LaunchFn{p, q, K, V, seq_lens, sel_idx, sel_cnt, softmax_scale, out, lse,
+                                part_o, part_ml, reinterpret_cast<int2*>(seg_rec), stream});
 }
 
 }  // namespace fx

@@ -7,7 +7,8 @@
  *   fx_build_summaries  pooled per-block key summaries (when blocks fill)
  *   fx_select           block scores against each GQA query group and per-kv-head
  *                       block selection (streaming / retrieval top-k / NOSA)
- *   fx_sparse_decode    split-K flash-decoding over the selected blocks only
+ *   fx_sparse_decode    flash-decoding over the selected blocks only, split evenly
+ *                       across the GPU
  *   fx_selection_delta  blocks added to / removed from the previous selection
  *
  * Sources, cited by page title and section:
@@ -52,7 +53,8 @@
  *
  * Ownership and ordering
  *   The caller owns every buffer, stream and the eviction mask.  A plan owns only
- *   a small device table (per-unit policies and an error word), allocated by
+ *   a small device table (per-unit policies, the list of scored units and an error
+ *   word), allocated by
  *   fx_plan_create and freed by fx_plan_destroy; the hot calls only read it (and
  *   set error bits).  The four hot calls never allocate, never synchronise and
  *   never copy between host and device: they enqueue kernels on `stream` and
@@ -118,7 +120,8 @@ typedef struct {
   int32_t t_cap;           /* tokens of capacity per unit, 1 .. 2^24, with t_cap * head_dim *
                               sizeof(elem) < 2^31 (else FX_E_UNSUPPORTED) */
   int32_t dtype;           /* FX_F32 or FX_BF16: element type of q, K, V, summaries, out */
-  int32_t split_tokens;    /* split-K chunk in tokens (a power of two, 64..2048), 0 = automatic */
+  int32_t split_tokens;    /* fewest selected tokens per decode workgroup (a power of two,
+                              64..2048), 0 = automatic (256) */
 } fx_plan_desc;
 
 /* Per-unit selection policy.  Blocks of one unit are `block` tokens (a power of
@@ -153,7 +156,9 @@ typedef struct fx_plan* fx_plan_t;
 
 /* Validate the shapes and the per-unit policies (host array of B*Hkv entries,
  * copied), compute the packed layouts, and allocate the plan's device table on
- * the current HIP device.  *out is set only on FX_OK. */
+ * the current HIP device; the decode split is sized for that device.  The most
+ * tokens all units can select together, sum over u of min(max_sel(u) * block(u),
+ * t_cap), must stay below 2^31 (else FX_E_UNSUPPORTED).  *out is set only on FX_OK. */
 fx_status fx_plan_create(const fx_plan_desc* desc, const fx_head_policy* host_policies,
                          fx_plan_t* out);
 /* Free the plan's device table.  NULL is a no-op.  Waits for nothing: the caller
@@ -167,7 +172,7 @@ size_t fx_evict_mask_bytes(fx_plan_t plan);    /* total mask words * 4 */
 size_t fx_workspace_bytes(fx_plan_t plan);     /* workspace for fx_select and fx_sparse_decode */
 int32_t fx_max_selected(fx_plan_t plan);       /* max_sel: row stride of sel_idx and delta lists */
 int64_t fx_unit_block_offset(fx_plan_t plan, int32_t unit);   /* block_off(u), -1 if out of range */
-int32_t fx_split_tokens(fx_plan_t plan);       /* the split-K chunk the plan uses */
+int32_t fx_split_tokens(fx_plan_t plan);       /* the split_tokens value the plan uses */
 
 const char* fx_status_string(fx_status status);
 
@@ -223,9 +228,12 @@ fx_status fx_select(fx_plan_t plan, const void* q, const void* summaries,
  * For each unit and each of its G query rows q: over the valid tokens t of the
  * selected blocks, s_t = softmax_scale * (q . K_t); out = sum_t e^{s_t - m} V_t / l
  * with m = max s_t and l = sum_t e^{s_t - m}; lse = m + ln l.  Computed as
- * split-K flash-decoding (float32 online softmax per chunk of selected tokens,
- * then a log-sum-exp merge of the chunks in chunk order in a second kernel, so
- * results do not depend on scheduling).  A unit with no valid token gets out = 0, lse = -inf.
+ * flash-decoding with a float32 online softmax: the units' selected tokens, laid end
+ * to end, are cut into as many equal segments (at least split_tokens long) as the
+ * GPU holds decode workgroups at once, one per workgroup; a unit cut by a segment
+ * boundary is finished by a log-sum-exp merge of its pieces in a second kernel, in
+ * piece order.  Results depend only on the inputs and the plan (on one device), not
+ * on scheduling.  A unit with no valid token gets out = 0, lse = -inf.
  * sel_idx / sel_cnt as written by fx_select (any ascending list of valid block
  * indices of the unit is accepted).  lse may be NULL.  workspace as for fx_select
  * (the two calls may share one workspace; they use disjoint parts of it). */
