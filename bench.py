@@ -4,7 +4,7 @@
 A step is one pass of the whole hot path over one batch of synthetic input:
   fx_build_summaries  (the newest full block of every unit, as when a block fills)
   fx_select           (scores + per-kv-head selection)
-  fx_sparse_decode    (split-K attention over the selected blocks + merge)
+  fx_sparse_decode    (attention over the selected blocks in equal segments + merge)
   fx_selection_delta  (against the previous step's selection)
 Inputs are resident in HBM before timing starts.  The default workload is the mixed
 serving batch (64 sequences of U{8192..131072} tokens, 32 q / 8 kv heads, d 128,
@@ -35,7 +35,7 @@ def log(msg: str) -> None:
 
 
 def algorithmic_bytes(w, max_sel, sel_idx, sel_cnt):
-    """The method's own HBM traffic for one step (split-K partials and scores excluded).
+    """The method's own HBM traffic for one step (decode partials and scores excluded).
 
     Per unit: KV = 2 d e N (N = valid tokens of the selected blocks); summaries read by
     scoring = n_full d e (retrieval / NOSA units); newest-block summary build = g d e read
@@ -150,7 +150,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixed_serving")
-    ap.add_argument("--split", type=int, default=0, help="split-K chunk (tokens), 0 = plan default")
+    ap.add_argument("--split", type=int, default=0, help="minimum decode segment (tokens), 0 = plan default")
     ap.add_argument("--flush", action="store_true",
                     help="overwrite 1 GiB between steps (outside the timed events)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
