@@ -71,7 +71,10 @@ def algorithmic_bytes(w, max_sel, sel_idx, sel_cnt):
         + 2 * w.num_units * max_sel * 4
     total = sum(parts.values())
     decode = parts["kv"] + n_q * d * e + parts["out"] + parts["lse"] + tot_cnt * 4
-    return total, decode, parts
+    # fx_select + fx_sparse_decode alone: no summary build, no delta.
+    sel_dec = (parts["kv"] + parts["summaries"] + parts["logits_mask"] + parts["q"] + parts["out"]
+               + parts["lse"] + w.num_units * max_sel * 4 + tot_cnt * 4)
+    return total, decode, sel_dec, parts
 
 
 def decode_source_hash() -> str:
@@ -151,8 +154,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixed_serving")
     ap.add_argument("--split", type=int, default=0, help="minimum decode segment (tokens), 0 = plan default")
-    ap.add_argument("--flush", action="store_true",
-                    help="overwrite 1 GiB between steps (outside the timed events)")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="skip the 1 GiB overwrite between steps (outside the timed events) "
+                         "that keeps the 256 MB Infinity Cache from holding the previous step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-reference", action="store_true",
@@ -192,7 +196,7 @@ def main() -> int:
     logits = inp.logits
     mask = A.evicted_mask if w.has_nosa else None
     fx.fx_build_summaries(plan, inp.K, inp.seq_lens, 0, INT32_MAX, A.summaries)   # prefill
-    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev) if args.flush else None
+    flush_buf = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
 
     cur, prev = A, Bsel
 
@@ -200,6 +204,7 @@ def main() -> int:
         nonlocal cur, prev
         q = qs[i % len(qs)]
         fx.fx_build_summaries(plan, inp.K, inp.seq_lens, -1, INT32_MAX, A.summaries)
+        ev_b1[i].record()
         fx.fx_select(plan, q, A.summaries, logits, mask, inp.seq_lens, cur.sel_idx, cur.sel_cnt,
                      A.workspace)
         ev_d0[i].record()
@@ -212,7 +217,14 @@ def main() -> int:
 
     n_ev = args.warmup + args.steps
     mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-    ev_s0, ev_s1, ev_d0, ev_d1 = mk(), mk(), mk(), mk()
+    ev_s0, ev_s1, ev_b1, ev_d0, ev_d1 = mk(), mk(), mk(), mk(), mk()
+    # Per-step selection statistics of multi-step (drifting query) workloads, copied out
+    # after each step's end event.
+    multi = len(qs) > 1
+    if multi:
+        hist_cnt = torch.zeros(n_ev, w.num_units, dtype=torch.int32, device=dev)
+        hist_add = torch.zeros_like(hist_cnt)
+        hist_rem = torch.zeros_like(hist_cnt)
     for i in range(args.warmup):
         ev_s0[i].record()
         step(i)
@@ -225,14 +237,57 @@ def main() -> int:
         ev_s0[i].record()
         step(i)
         ev_s1[i].record()
+        if multi:
+            hist_cnt[i].copy_(prev.sel_cnt)      # prev: this step's selection after the swap
+            hist_add[i].copy_(A.added_cnt)
+            hist_rem[i].copy_(A.removed_cnt)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
-    step_ms = [ev_s0[i].elapsed_time(ev_s1[i]) for i in range(args.warmup, n_ev)]
-    dec_ms = [ev_d0[i].elapsed_time(ev_d1[i]) for i in range(args.warmup, n_ev)]
+    timed = range(args.warmup, n_ev)
+    step_ms = [ev_s0[i].elapsed_time(ev_s1[i]) for i in timed]
+    dec_ms = [ev_d0[i].elapsed_time(ev_d1[i]) for i in timed]
+    phases = {
+        "build": [ev_s0[i].elapsed_time(ev_b1[i]) for i in timed],
+        "select": [ev_b1[i].elapsed_time(ev_d0[i]) for i in timed],
+        "decode": dec_ms,
+        "delta": [ev_d1[i].elapsed_time(ev_s1[i]) for i in timed],
+        "select_decode": [ev_b1[i].elapsed_time(ev_d1[i]) for i in timed],
+    }
     ms_per_step = float(np.mean(step_ms))
     dec_avg = float(np.mean(dec_ms))
     if fx.fx_read_error(plan) != 0:
         raise SystemExit("device error word set during the benchmark")
+
+    # Attainable-bandwidth reference: a plain streaming read of 2 GiB of the K cache.
+    ref_bytes = min(2 << 30, inp.K.numel() * inp.K.element_size()) // 16 * 16
+    ref_src = inp.K.view(torch.uint8).reshape(-1)[:ref_bytes]
+    sink = torch.empty(fx.load_library().fx_stream_read_sink_words(ref_bytes), dtype=torch.int32,
+                       device=dev)
+    for _ in range(2):
+        fx.fx_stream_read(ref_src, sink)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ref_ms = []
+    for _ in range(5):
+        if flush_buf is not None:
+            flush_buf.fill_(1)
+        e0.record()
+        fx.fx_stream_read(ref_src, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        ref_ms.append(e0.elapsed_time(e1))
+    stream_gbs = ref_bytes / (float(np.median(ref_ms)) * 1e-3) / 1e9
+
+    drift = None
+    if multi:
+        c = hist_cnt[args.warmup:].cpu().numpy().astype(np.float64)
+        a = hist_add[args.warmup:].cpu().numpy().astype(np.float64)
+        r = hist_rem[args.warmup:].cpu().numpy().astype(np.float64)
+        with np.errstate(invalid="ignore", divide="ignore"):
+            gamma = np.where(c > 0, (c - a) / c, 1.0)
+        drift = {"added_mean": round(float(a.mean()), 3), "added_max": int(a.max()),
+                 "removed_mean": round(float(r.mean()), 3), "removed_max": int(r.max()),
+                 "locality_min": round(float(gamma.min()), 4),
+                 "steps_per_query_cycle": len(qs)}
 
     if args.copy_reference:
         src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
@@ -243,14 +298,21 @@ def main() -> int:
 
     sel_idx = prev.sel_idx.cpu().numpy()      # the last step's selection
     sel_cnt = prev.sel_cnt.cpu().numpy()
-    total_b, dec_b, parts = algorithmic_bytes(w, plan.max_selected, sel_idx, sel_cnt)
+    total_b, dec_b, sd_b, parts = algorithmic_bytes(w, plan.max_selected, sel_idx, sel_cnt)
     value = total_b / (ms_per_step * 1e-3) / 1e9
     achieved = dec_b / (dec_avg * 1e-3) / 1e9
+    sd_med = float(np.median(phases["select_decode"]))
+    sd_gbs = sd_b / (sd_med * 1e-3) / 1e9
     log(f"[bench] {w.name}: {ms_per_step * 1e3:.1f} us/step (p10 {np.percentile(step_ms, 10) * 1e3:.1f},"
         f" p90 {np.percentile(step_ms, 90) * 1e3:.1f}), decode {dec_avg * 1e3:.1f} us; "
         f"{total_b / 1e6:.1f} MB/step -> {value:.0f} GB/s ({100 * value / HBM_PEAK_GBS:.1f}% of peak); "
         f"decode {achieved:.0f} GB/s; wall {wall / args.steps * 1e3:.3f} ms/step")
     log(f"[bench] bytes/step: " + ", ".join(f"{k} {v / 1e6:.2f} MB" for k, v in parts.items()))
+    log(f"[bench] phase medians (us): " + ", ".join(
+        f"{k} {float(np.median(v)) * 1e3:.1f}" for k, v in phases.items())
+        + f"; select+decode {sd_gbs:.0f} GB/s; streaming-read reference {stream_gbs:.0f} GB/s")
+    if drift:
+        log(f"[bench] selection drift: {drift}")
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -263,7 +325,7 @@ def main() -> int:
         "head_dim": w.head_dim, "t_cap": w.t_cap,
         "seq_lens": "U{8192..131072}" if w.name == "mixed_serving" else w.seq_lens[0],
         "blocks": sorted({p.block for p in w.policies}), "split_tokens": plan.split_tokens,
-        "cache_flush_between_steps": bool(args.flush),
+        "cache_flush_between_steps": not args.no_flush,
     }
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
@@ -281,7 +343,15 @@ def main() -> int:
                      "alg_bytes_per_launch": int(dec_b), "avg_launch_us": round(dec_avg * 1e3, 2),
                      "k_decode_sha256_16": decode_source_hash()},
         "cpu_baseline": cpu,
+        "select_decode": {"us_median": round(sd_med * 1e3, 2), "alg_bytes": int(sd_b),
+                          "achieved": round(sd_gbs, 1), "unit": "GB/s",
+                          "frac": round(sd_gbs / HBM_PEAK_GBS, 4)},
+        "phases_us_median": {k: round(float(np.median(v)) * 1e3, 2) for k, v in phases.items()},
+        "stream_read_reference": {"achieved": round(stream_gbs, 1), "unit": "GB/s",
+                                  "bytes": int(ref_bytes)},
     }
+    if drift:
+        line["selection_drift"] = drift
     print(json.dumps(line), flush=True)
     return 0
 

@@ -23,6 +23,7 @@ __all__ = [
     "FxError", "Plan", "library_path", "load_library",
     "fx_plan_create", "fx_plan_destroy", "fx_build_summaries", "fx_select",
     "fx_sparse_decode", "fx_selection_delta", "fx_read_error", "fx_status_string",
+    "fx_stream_read",
     "StepBuffers", "allocate_step_buffers",
 ]
 
@@ -89,6 +90,8 @@ def load_library(path: Optional[str] = None):
         "fx_sparse_decode": (_I32, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P,
                                     ctypes.c_size_t, _P]),
         "fx_selection_delta": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+        "fx_stream_read_sink_words": (ctypes.c_size_t, [ctypes.c_size_t]),
+        "fx_stream_read": (_I32, [_P, ctypes.c_size_t, _P, _P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -263,6 +266,17 @@ def fx_selection_delta(plan: Plan, prev_idx: torch.Tensor, prev_cnt: torch.Tenso
         _ptr(added, "added", i32, n), _ptr(added_cnt, "added_cnt", i32, u),
         _ptr(removed, "removed", i32, n), _ptr(removed_cnt, "removed_cnt", i32, u),
         _stream(stream)))
+
+
+def fx_stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Read all of `src` once (the streaming-read bandwidth reference); sink: int32 GPU
+    tensor of at least fx_stream_read_sink_words(src bytes) elements."""
+    lib = load_library()
+    nbytes = src.numel() * src.element_size()
+    words = lib.fx_stream_read_sink_words(nbytes)
+    _check("fx_stream_read", lib.fx_stream_read(_ptr(src, "src"), nbytes,
+                                                _ptr(sink, "sink", torch.int32, words),
+                                                _stream(stream)))
 
 
 @dataclass

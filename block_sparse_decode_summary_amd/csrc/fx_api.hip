@@ -264,6 +264,21 @@ fx_status fx_read_error(fx_plan_t p, uint32_t* host_word) {
   return FX_OK;
 }
 
+size_t fx_stream_read_sink_words(size_t bytes) {
+  return (size_t)((bytes + fx::kStreamReadSpan - 1) / fx::kStreamReadSpan);
+}
+
+fx_status fx_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  if (!req(src, 16) || !req(sink, 4) || bytes == 0 || bytes % 16 != 0 ||
+      fx_stream_read_sink_words(bytes) > (size_t)INT32_MAX)
+    return FX_E_INVALID;
+  try {
+    return hip_status(fx::launch_stream_read(src, bytes, sink, stream));
+  } catch (...) {
+    return FX_E_HIP;
+  }
+}
+
 fx_status fx_build_summaries(fx_plan_t p, const void* K, const int32_t* seq_lens,
                              int32_t block_begin, int32_t block_end, void* summaries,
                              hipStream_t stream) {

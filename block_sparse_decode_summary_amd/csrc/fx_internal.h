@@ -18,6 +18,7 @@ constexpr int kMaxSplit = 2048;       // largest minimum decode segment; also th
                                       // whose block indices one LDS list holds
 constexpr int kMinSplit = 64;
 constexpr int kAutoSplit = 256;       // minimum decode segment when the caller passes 0
+constexpr uint64_t kStreamReadSpan = 1ull << 20;   // bytes per workgroup of fx_stream_read
 constexpr int kMaxTcap = 1 << 24;
 constexpr int kTopkRegBlocks = 8192;   // selection keeps keys in registers up to this n_cap
 
@@ -95,7 +96,8 @@ hipError_t launch_decode(const fx_plan* p, const void* q, const void* K, const v
                          const int32_t* seq_lens, const int32_t* sel_idx,
                          const int32_t* sel_cnt, float softmax_scale, void* out, float* lse,
                          float* part_o, float* part_ml, int32_t* seg_rec, hipStream_t stream);
-int decode_grid(const fx_plan* p);   // resident decode workgroups on the current device (0: error)
+int decode_grid(const fx_plan* p);
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);   // resident decode workgroups on the current device (0: error)
 hipError_t launch_delta(const fx_plan* p, const int32_t* prev_idx, const int32_t* prev_cnt,
                         const int32_t* cur_idx, const int32_t* cur_cnt, int32_t* added,
                         int32_t* added_cnt, int32_t* removed, int32_t* removed_cnt,

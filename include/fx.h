@@ -180,6 +180,15 @@ const char* fx_status_string(fx_status status);
  * the current device (a debugging / harness call, not for the hot loop). */
 fx_status fx_read_error(fx_plan_t plan, uint32_t* host_word);
 
+/* Measurement utility, not part of the decode path: the attainable streaming-read
+ * bandwidth reference.  Reads the `bytes` bytes at `src` (device memory, 16-byte
+ * aligned) once with 16-byte nontemporal loads, one workgroup per 1 MiB span, and
+ * writes the XOR of each span to sink[span] (fx_stream_read_sink_words(bytes) uint32
+ * words of device memory), so the reads cannot be removed.  Enqueued on `stream`;
+ * allocates nothing. */
+size_t fx_stream_read_sink_words(size_t bytes);
+fx_status fx_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 /* [NOSA-DE] Methodik §1, bullet "Blockweise Implementierung" (two-stage pooling:
  * mean inside sub-blocks, then max at block level); Methodik §2, bullet "Kernel
  * Fusion" (pooling runs inside a fused kernel).
