@@ -154,6 +154,9 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixed_serving")
     ap.add_argument("--split", type=int, default=0, help="minimum decode segment (tokens), 0 = plan default")
+    ap.add_argument("--grow", action="store_true",
+                    help="decode loop: append one token to every sequence before each step "
+                         "(outside the timed events; t_cap grows by the number of steps)")
     ap.add_argument("--no-flush", action="store_true",
                     help="skip the 1 GiB overwrite between steps (outside the timed events) "
                          "that keeps the 256 MB Infinity Cache from holding the previous step")
@@ -173,11 +176,13 @@ def main() -> int:
     import torch
 
     import block_sparse_decode_summary_amd as fx
-    from workloads import WORKLOAD_NAMES, generate, get_workload, query_at_step
+    from workloads import WORKLOAD_NAMES, append_tokens, generate, get_workload, query_at_step
 
     if args.workload not in WORKLOAD_NAMES:
         raise SystemExit(f"unknown workload {args.workload}; one of {WORKLOAD_NAMES}")
     w = get_workload(args.workload)
+    if args.grow:
+        w = w.replace(t_cap=w.t_cap + args.warmup + args.steps)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     t0 = time.time()
@@ -199,6 +204,7 @@ def main() -> int:
     flush_buf = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
 
     cur, prev = A, Bsel
+    lens = list(w.seq_lens)
 
     def step(i):
         nonlocal cur, prev
@@ -226,12 +232,16 @@ def main() -> int:
         hist_add = torch.zeros_like(hist_cnt)
         hist_rem = torch.zeros_like(hist_cnt)
     for i in range(args.warmup):
+        if args.grow:
+            lens = append_tokens(inp, lens, i + 1)
         ev_s0[i].record()
         step(i)
         ev_s1[i].record()
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for i in range(args.warmup, n_ev):
+        if args.grow:
+            lens = append_tokens(inp, lens, i + 1)
         if flush_buf is not None:
             flush_buf.fill_(i & 0xFF)
         ev_s0[i].record()
@@ -298,7 +308,8 @@ def main() -> int:
 
     sel_idx = prev.sel_idx.cpu().numpy()      # the last step's selection
     sel_cnt = prev.sel_cnt.cpu().numpy()
-    total_b, dec_b, sd_b, parts = algorithmic_bytes(w, plan.max_selected, sel_idx, sel_cnt)
+    w_last = w.replace(seq_lens=tuple(lens))      # the lengths of the last timed step
+    total_b, dec_b, sd_b, parts = algorithmic_bytes(w_last, plan.max_selected, sel_idx, sel_cnt)
     value = total_b / (ms_per_step * 1e-3) / 1e9
     achieved = dec_b / (dec_avg * 1e-3) / 1e9
     sd_med = float(np.median(phases["select_decode"]))
@@ -326,6 +337,7 @@ def main() -> int:
         "seq_lens": "U{8192..131072}" if w.name == "mixed_serving" else w.seq_lens[0],
         "blocks": sorted({p.block for p in w.policies}), "split_tokens": plan.split_tokens,
         "cache_flush_between_steps": not args.no_flush,
+        "decode_loop_growth": bool(args.grow),
     }
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,

@@ -4,6 +4,7 @@ Bar: summaries, scores, selected indices, eviction masks and deltas bit-exact;
 out within |d| <= atol + rtol |ref| (bf16: rtol 2e-2, atol 1e-2; fp32: 1e-4, 1e-4)
 against the oracle's float64 value; lse within rtol 1e-5, atol 1e-4.
 """
+import dataclasses
 import math
 
 import numpy as np
@@ -14,7 +15,8 @@ import block_sparse_decode_summary_amd as fx
 from oracle.delta import locality, selection_delta
 from oracle.step import unit_step
 from workloads import (HeadPolicy, MODE_NOSA, MODE_RETRIEVAL, MODE_STREAMING, WORKLOAD_NAMES,
-                       Workload, generate, get_workload, query_at_step, small_workload, unit_arrays)
+                       Workload, append_tokens, generate, get_workload, query_at_step,
+                       small_workload, unit_arrays)
 
 from gpu_harness import (INT32_MAX, GpuView, compare_unit, make_plan, oracle_unit,
                          run_select_decode, say, softmax_scale, assert_close, TOL)
@@ -233,6 +235,63 @@ def test_equal_values_take_lowest_indices():
     assert list(gv.unit(1).sel) == list(range(0, 160)) + [n_tot - 1]
     ev = gv.evicted(1)
     assert not ev[:90].any() and ev[90:n_full].all() and not ev[n_full:].any()
+    assert fx.fx_read_error(plan) == 0
+
+
+def test_growing_context_decode_loop():
+    """The decode loop: every step appends one token to every sequence, the newest full
+    block's summary is (re)built, new full blocks become score and eviction candidates,
+    and the eviction mask carries NOSA's state from step to step.  Each step is checked
+    against the oracle on the grown inputs: summaries, scores, selections and the mask
+    bit-exact, outputs and deltas as everywhere else."""
+    g = 16
+    pols = [HeadPolicy(MODE_RETRIEVAL, block=g, sub_block=4, budget=float(np.float32(0.1)),
+                       force_sink=1, force_last=1),
+            HeadPolicy(MODE_NOSA, block=g, sub_block=8, top_k=3, k_evict=5),
+            HeadPolicy(MODE_STREAMING, block=g, sub_block=16, sink_tokens=4, local_tokens=40)]
+    lens = [16 * 12 + 13, 16 * 7 + 15, 16 * 30]     # three phases within a block
+    steps = 40
+    w0 = _custom("grow", 3, 6, 3, 64, "bf16", max(lens) + steps + 8, lens, pols * 3)
+    w0 = w0.replace(drift=(0.9, 0.44))
+    inp = generate(w0, DEV)
+    plan = make_plan(w0)
+    bufs = fx.allocate_step_buffers(plan, DEV)
+    fx.fx_build_summaries(plan, inp.K, inp.seq_lens, 0, INT32_MAX, bufs.summaries)   # prefill
+    evicted = {u: None for u in range(w0.num_units)}
+    prev = {u: np.zeros(0, np.int64) for u in range(w0.num_units)}
+    filled = 0
+    for t in range(steps):
+        if t > 0:
+            old = lens
+            lens = append_tokens(inp, lens, t)
+            filled += sum(1 for a, b in zip(old, lens) if b % g == 0 and b != a)
+        w = w0.replace(seq_lens=tuple(lens))
+        it = dataclasses.replace(inp, workload=w)
+        q = query_at_step(w0, t, DEV)
+        fx.fx_build_summaries(plan, inp.K, inp.seq_lens, -1, INT32_MAX, bufs.summaries)
+        bufs.prev_idx.copy_(bufs.sel_idx)
+        bufs.prev_cnt.copy_(bufs.sel_cnt)
+        run_select_decode(plan, bufs, it, q, build=False)
+        fx.fx_selection_delta(plan, bufs.prev_idx, bufs.prev_cnt, bufs.sel_idx, bufs.sel_cnt,
+                              bufs.added, bufs.added_cnt, bufs.removed, bufs.removed_cnt)
+        gv = GpuView(plan, bufs, w)
+        added, added_cnt = bufs.added.cpu().numpy(), bufs.added_cnt.cpu().numpy()
+        removed, removed_cnt = bufs.removed.cpu().numpy(), bufs.removed_cnt.cpu().numpy()
+        for u in range(w.num_units):
+            ref = oracle_unit(it, u, q, evicted[u])
+            compare_unit(w, u, gv, ref)
+            if w.policies[u].mode == MODE_NOSA:
+                n_full = lens[u // w.num_kv_heads] // g
+                got_ev = gv.evicted(u)
+                assert np.array_equal(got_ev[:n_full], ref.evicted[:n_full]), f"unit {u} mask step {t}"
+                assert not got_ev[n_full:].any()
+                # Over all block slots: blocks that fill later start out not evicted.
+                evicted[u] = np.pad(ref.evicted, (0, w.n_cap(u) - len(ref.evicted)))
+            a_ref, r_ref = selection_delta(prev[u], ref.sel)
+            assert list(added[u, :added_cnt[u]]) == list(a_ref), f"unit {u} added, step {t}"
+            assert list(removed[u, :removed_cnt[u]]) == list(r_ref), f"unit {u} removed, step {t}"
+            prev[u] = ref.sel
+    assert filled >= 6, "the loop should fill several blocks"
     assert fx.fx_read_error(plan) == 0
 
 

@@ -4,7 +4,7 @@ import pytest
 import torch
 
 from workloads import (WORKLOAD_NAMES, MODE_NOSA, MODE_RETRIEVAL, MODE_STREAMING,
-                       generate, get_workload, query_at_step, small_workload)
+                       append_tokens, generate, get_workload, query_at_step, small_workload)
 
 
 def test_full_workload_shapes():
@@ -88,3 +88,27 @@ def test_query_drift():
     c1 = torch.nn.functional.cosine_similarity(q0.flatten(), q1.flatten(), dim=0)
     c5 = torch.nn.functional.cosine_similarity(q0.flatten(), q5.flatten(), dim=0)
     assert 0.8 < c1 < 0.95 and c5 < c1          # correlation 0.9 per step, decaying
+
+
+def test_append_tokens_writes_one_seeded_row_per_sequence():
+    w = small_workload("mixed_serving")
+    w = w.replace(t_cap=max(w.seq_lens) + 4)
+    a, b = generate(w, "cpu"), generate(w, "cpu")
+    lens = list(w.seq_lens)
+    K0 = a.K.clone()
+    new_a = append_tokens(a, lens, 3)
+    new_b = append_tokens(b, lens, 3)
+    assert new_a == [T + 1 for T in lens] == new_b
+    assert a.seq_lens.tolist() == new_a
+    assert torch.equal(a.K, b.K) and torch.equal(a.V, b.V)          # seeded
+    for bi, T in enumerate(lens):
+        assert torch.any(a.K[bi, :, T] != 0) and torch.any(a.V[bi, :, T] != 0)
+        assert torch.equal(a.K[bi, :, :T], K0[bi, :, :T])            # earlier rows untouched
+        assert not torch.any(a.K[bi, :, T + 1:] != 0)
+    c = generate(w, "cpu")
+    append_tokens(c, lens, 4)                                        # another step, other rows
+    assert not torch.equal(a.K, c.K)
+    full = w.replace(t_cap=max(lens))                                # sequences at capacity stay
+    d = generate(full, "cpu")
+    longest = int(np.argmax(lens))
+    assert append_tokens(d, lens, 0)[longest] == lens[longest]

@@ -18,10 +18,10 @@ Workloads follow the five shapes this build is measured on:
 """
 from .configs import (HeadPolicy, Workload, get_workload, small_workload,
                       WORKLOAD_NAMES, MODE_RETRIEVAL, MODE_STREAMING, MODE_NOSA)
-from .generate import Inputs, generate, query_at_step, unit_arrays
+from .generate import Inputs, append_tokens, generate, query_at_step, unit_arrays
 
 __all__ = [
     "HeadPolicy", "Workload", "get_workload", "small_workload", "WORKLOAD_NAMES",
     "MODE_RETRIEVAL", "MODE_STREAMING", "MODE_NOSA",
-    "Inputs", "generate", "query_at_step", "unit_arrays",
+    "Inputs", "append_tokens", "generate", "query_at_step", "unit_arrays",
 ]

@@ -25,7 +25,7 @@ MODE_NOSA = 2
 _MODE_NAMES = {MODE_RETRIEVAL: "retrieval", MODE_STREAMING: "streaming", MODE_NOSA: "nosa"}
 
 # Sub-stream purposes for np.random.SeedSequence([seed, purpose, ...]).
-P_POLICY, P_QUERY, P_KV, P_NEEDLE, P_LOGITS, P_DRIFT, P_LENS = 1, 2, 3, 4, 5, 6, 7
+P_POLICY, P_QUERY, P_KV, P_NEEDLE, P_LOGITS, P_DRIFT, P_LENS, P_APPEND = 1, 2, 3, 4, 5, 6, 7, 8
 
 
 @dataclass(frozen=True)

@@ -16,6 +16,9 @@ tensors):
        then rounded to the workload dtype.  Rows at or beyond a sequence's length
        stay zero.
 * eviction logits (workloads with NOSA heads): N(0, 1) float32 per block slot.
+* decode-loop growth (append_tokens): step t appends to sequence b one key row and one
+  value row per kv head, N(0, 1) from torch's generator seeded by (seed, append, b, t),
+  rounded to the workload dtype, at position seq_len(b).
 
 Sub-streams come from np.random.SeedSequence([seed, purpose, ...]) so that any
 (sequence, kv head) can be regenerated on its own.
@@ -29,7 +32,7 @@ import numpy as np
 import torch
 
 from .configs import (Workload, MODE_NOSA, P_QUERY, P_KV, P_NEEDLE, P_LOGITS, P_DRIFT,
-                      _rng)
+                      P_APPEND, _rng)
 
 
 def storage_dtype(w: Workload) -> torch.dtype:
@@ -135,6 +138,27 @@ def generate(w: Workload, device="cpu") -> Inputs:
     seq_lens = torch.tensor(w.seq_lens, dtype=torch.int32, device=device)
     return Inputs(workload=w, device=device, q=q, K=K, V=V, seq_lens=seq_lens,
                   logits=logits, needles=needles)
+
+
+def append_tokens(inp: Inputs, lens: List[int], step: int) -> List[int]:
+    """Append one decode token to every sequence shorter than t_cap (seeded key and
+    value rows at position lens[b]) and store the new lengths in inp.seq_lens.  Returns
+    the new host-side lengths; inp.workload keeps the lengths it was generated with."""
+    w = inp.workload
+    new = list(lens)
+    for b in range(w.batch):
+        T = lens[b]
+        if T >= w.t_cap:
+            continue
+        gen = torch.Generator(device=inp.device)
+        gen.manual_seed(_seed32(w.seed, P_APPEND, b, step))
+        kv = torch.randn((2, w.num_kv_heads, w.head_dim), generator=gen, device=inp.device,
+                         dtype=torch.float32)
+        inp.K[b, :, T] = kv[0].to(inp.K.dtype)
+        inp.V[b, :, T] = kv[1].to(inp.V.dtype)
+        new[b] = T + 1
+    inp.seq_lens.copy_(torch.tensor(new, dtype=torch.int32, device=inp.device))
+    return new
 
 
 def unit_arrays(inp: Inputs, b: int, h: int, q: Optional[torch.Tensor] = None
