@@ -15,11 +15,11 @@ from typing import Optional
 
 import numpy as np
 
-from .attention import attend, selected_tokens
+from .attention import attend, selected_tokens, token_bias
 from .numerics import round_to_storage
 from .pooling import block_summaries
 from .scoring import block_scores
-from .selection import MODE_STREAMING, select_unit
+from .selection import MODE_NOSA, MODE_STREAMING, select_unit
 
 
 @dataclass
@@ -36,11 +36,18 @@ class UnitResult:
 def unit_step(pol, T: int, dtype: str, q_rows: np.ndarray, K: np.ndarray, V: np.ndarray,
               scale: float, logits: Optional[np.ndarray] = None,
               evicted: Optional[np.ndarray] = None,
-              summaries: Optional[np.ndarray] = None) -> UnitResult:
-    """q_rows float64 [G][d]; K, V float64 [T][d] (the unit's valid rows)."""
+              summaries: Optional[np.ndarray] = None, ed: bool = False) -> UnitResult:
+    """q_rows float64 [G][d]; K, V float64 [T][d] (the unit's valid rows).
+
+    ``ed``: a NOSA unit adds each selected block's eviction logit (``logits``, one per
+    block slot of the unit) to its tokens' attention logits ([NOSA-DE] Methodik §1,
+    "ED-DMA"); other modes have no eviction head and are unaffected."""
     S = block_summaries(K, pol.block, pol.sub_block, dtype) if summaries is None else summaries
     scores = None if pol.mode == MODE_STREAMING else block_scores(q_rows, S)
     sel, ev = select_unit(pol, T, scores, logits, evicted)
     tok = selected_tokens(sel, pol.block, T)
-    out, lse = attend(q_rows, K[tok], V[tok], scale)
+    bias = None
+    if ed and pol.mode == MODE_NOSA:
+        bias = token_bias(sel, pol.block, T, logits)
+    out, lse = attend(q_rows, K[tok], V[tok], scale, bias)
     return UnitResult(S, scores, sel, ev, round_to_storage(out, dtype), out, lse)

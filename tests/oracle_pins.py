@@ -415,6 +415,80 @@ def check_attention(attend, selected_tokens, merge_partials, partial):
         assert np.allclose(o2, out, rtol=1e-12, atol=1e-12) and np.allclose(l2, lse, rtol=1e-12)
 
 
+def _dense_additive(q, K, V, keep_tokens, bias_tokens, scale):
+    """Reference: torch scaled_dot_product_attention in float64 with a FLOAT mask, which the
+    library adds to the scaled logits: the bias on the kept tokens, -inf elsewhere."""
+    T = K.shape[0]
+    mask = torch.full((q.shape[0], T), -math.inf, dtype=torch.float64)
+    mask[:, torch.from_numpy(np.asarray(keep_tokens, dtype=np.int64))] = torch.from_numpy(
+        np.asarray(bias_tokens, dtype=np.float64))[None, :]
+    out = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q)[None], torch.from_numpy(K)[None], torch.from_numpy(V)[None],
+        attn_mask=mask[None], scale=scale)
+    return out[0].numpy()
+
+
+def check_biased_attention(attend, token_bias, selected_tokens, merge_partials, partial):
+    """[NOSA-DE] Methodik §1, "ED-DMA", read as an additive pre-softmax term per block."""
+    # token_bias by hand: g = 4, T = 10, blocks 0 and 2 (block 2 holds tokens 8, 9 only).
+    assert list(token_bias(np.array([0, 2]), 4, 10, np.array([0.5, -1.0, 2.0]))) == \
+        [0.5] * 4 + [2.0] * 2
+    assert len(token_bias(np.zeros(0, np.int64), 4, 10, np.zeros(3))) == 0
+    # Two tokens with equal keys, values 0 and 1, bias (0, b): out = sigmoid(b),
+    # lse = ln(1 + e^b) (the key logits are 0).
+    for b in (0.7, -2.0, 5.5):
+        out, lse = attend(np.array([[1.0]]), np.zeros((2, 1)), np.array([[0.0], [1.0]]), 1.0,
+                          np.array([0.0, b]))
+        assert abs(out[0, 0] - 1.0 / (1.0 + math.exp(-b))) < 1e-15
+        assert abs(lse[0] - math.log1p(math.exp(b))) < 1e-14
+
+    rng = np.random.default_rng(21)
+    G, d, T, g = 4, 32, 203, 16
+    q = rng.standard_normal((G, d))
+    K = rng.standard_normal((T, d))
+    V = rng.standard_normal((T, d))
+    scale = 1 / math.sqrt(d)
+    sel = np.array([0, 3, 4, 9, 12])               # 12 is the partial last block
+    logits = rng.standard_normal(-(-T // g))
+    tok = selected_tokens(sel, g, T)
+    bias = token_bias(sel, g, T, logits)
+    out, lse = attend(q, K[tok], V[tok], scale, bias)
+    # The library's additive float mask.
+    assert np.allclose(out, _dense_additive(q, K, V, tok, bias, scale), rtol=1e-12, atol=1e-12)
+    s = (q @ K[tok].T) * scale + bias[None, :]
+    assert np.allclose(lse, np.log(np.exp(s).sum(axis=1)), rtol=1e-12)
+    # A bias of ln 2 (ln 3) on one block weighs like that block's tokens present twice
+    # (three times) without a bias.
+    for reps in (2, 3):
+        bl = np.zeros_like(logits)
+        bl[4] = math.log(reps)
+        bo, bls = attend(q, K[tok], V[tok], scale, token_bias(sel, g, T, bl))
+        dup = np.concatenate([tok] + [np.arange(4 * g, 5 * g)] * (reps - 1))
+        do, dls = attend(q, K[dup], V[dup], scale)
+        assert np.allclose(bo, do, rtol=1e-12, atol=1e-12) and np.allclose(bls, dls, rtol=1e-12)
+    # A constant bias leaves out unchanged and shifts lse by that constant; zero is no bias.
+    oc, lc = attend(q, K[tok], V[tok], scale, np.full(len(tok), 1.75))
+    o0, l0 = attend(q, K[tok], V[tok], scale)
+    assert np.allclose(oc, o0, rtol=1e-12, atol=1e-12) and np.allclose(lc, l0 + 1.75, rtol=1e-12)
+    oz, lz = attend(q, K[tok], V[tok], scale, np.zeros(len(tok)))
+    assert np.array_equal(oz, o0) and np.array_equal(lz, l0)
+    # A very negative bias on a block removes it.
+    bl = logits.copy()
+    bl[3] = -1e4
+    on, ln_ = attend(q, K[tok], V[tok], scale, token_bias(sel, g, T, bl))
+    keep = sel[sel != 3]
+    tk = selected_tokens(keep, g, T)
+    ok, lk = attend(q, K[tk], V[tk], scale, token_bias(keep, g, T, bl))
+    assert np.allclose(on, ok, rtol=1e-12, atol=1e-12) and np.allclose(ln_, lk, rtol=1e-12)
+    # split-K with the bias: merging partials over any split equals the whole.
+    for cuts in ([50], [1, 2, 90], [0, 150, 150]):
+        edges = [0] + cuts + [len(tok)]
+        parts = [partial(q, K[tok[a:b]], V[tok[a:b]], scale, bias[a:b])
+                 for a, b in zip(edges[:-1], edges[1:])]
+        o2, l2 = merge_partials(parts)
+        assert np.allclose(o2, out, rtol=1e-12, atol=1e-12) and np.allclose(l2, lse, rtol=1e-12)
+
+
 # ----------------------------------------------------------------------------------------
 # delta
 # ----------------------------------------------------------------------------------------

@@ -292,6 +292,64 @@ def test_merge_mutant():
                   _merge_no_rescale, attention.partial)
 
 
+def _attend_bias_scaled(q, K, V, scale, bias=None):       # (q.k + b) * scale
+    return attention.attend(q, K, V, scale, None if bias is None else np.asarray(bias) * scale)
+
+
+def _attend_bias_ignored(q, K, V, scale, bias=None):
+    return attention.attend(q, K, V, scale)
+
+
+def _attend_bias_negated(q, K, V, scale, bias=None):
+    return attention.attend(q, K, V, scale, None if bias is None else -np.asarray(bias))
+
+
+def _attend_bias_after_exp(q, K, V, scale, bias=None):    # weights scaled by b, not e^b
+    if bias is None or len(bias) == 0:
+        return attention.attend(q, K, V, scale)
+    s = (np.asarray(q) @ np.asarray(K).T) * scale
+    p = np.exp(s - s.max(axis=1, keepdims=True)) * np.asarray(bias)[None, :]
+    l = p.sum(axis=1, keepdims=True)
+    return (p @ np.asarray(V)) / l, s.max(axis=1) + np.log(np.abs(l[:, 0]))
+
+
+def _partial_bias_ignored(q, K, V, scale, bias=None):
+    return attention.partial(q, K, V, scale)
+
+
+def _token_bias_by_position(sel, g, T, logits):           # b indexed by selection rank
+    sel = np.asarray(sel)
+    parts = [np.full(min((j + 1) * g, T) - j * g, float(logits[i])) for i, j in enumerate(sel)]
+    return np.concatenate(parts) if parts else np.zeros(0)
+
+
+def _token_bias_full_blocks(sel, g, T, logits):           # ignores the partial last block
+    parts = [np.full(g, float(logits[j])) for j in np.asarray(sel)]
+    return np.concatenate(parts) if parts else np.zeros(0)
+
+
+@pytest.mark.parametrize("which", ["scaled", "ignored", "negated", "after_exp", "partial",
+                                   "by_position", "full_blocks"])
+def test_biased_attention_mutants(which):
+    att, tb, part = attention.attend, attention.token_bias, attention.partial
+    if which == "scaled":
+        att = _attend_bias_scaled
+    elif which == "ignored":
+        att = _attend_bias_ignored
+    elif which == "negated":
+        att = _attend_bias_negated
+    elif which == "after_exp":
+        att = _attend_bias_after_exp
+    elif which == "partial":
+        part = _partial_bias_ignored
+    elif which == "by_position":
+        tb = _token_bias_by_position
+    else:
+        tb = _token_bias_full_blocks
+    assert _fails(pins.check_biased_attention, att, tb, attention.selected_tokens,
+                  attention.merge_partials, part)
+
+
 # ---- delta ----------------------------------------------------------------------------
 
 def _delta_swapped(prev, cur):

@@ -54,6 +54,38 @@ def test_attention():
                          attention.merge_partials, attention.partial)
 
 
+def test_biased_attention():
+    pins.check_biased_attention(attention.attend, attention.token_bias, attention.selected_tokens,
+                                attention.merge_partials, attention.partial)
+
+
+def test_unit_step_ed_biases_nosa_units_only():
+    """ED-DMA: a NOSA unit's tokens carry their block's eviction logit; the other modes
+    have no eviction head, so the switch changes nothing for them."""
+    rng = np.random.default_rng(22)
+    G, d, T, g = 2, 16, 150, 16
+    q = pins.random_bf16_values(rng, (G, d))
+    K = pins.random_bf16_values(rng, (T, d))
+    V = pins.random_bf16_values(rng, (T, d))
+    logits = rng.standard_normal(-(-T // g)).astype(np.float32)
+    scale = d ** -0.5
+    for pol in (pins.Pol(mode=0, block=g, sub_block=4, top_k=3, force_sink=1, force_last=1),
+                pins.Pol(mode=1, block=g, sub_block=4, sink_tokens=16, local_tokens=40)):
+        a = unit_step(pol, T, "bf16", q, K, V, scale, logits=logits)
+        b = unit_step(pol, T, "bf16", q, K, V, scale, logits=logits, ed=True)
+        assert np.array_equal(a.out_exact, b.out_exact) and np.array_equal(a.lse, b.lse)
+    pol = pins.Pol(mode=2, block=g, sub_block=4, top_k=2, k_evict=3, force_sink=1, force_last=1)
+    ev = np.zeros(-(-T // g), dtype=bool)
+    a = unit_step(pol, T, "bf16", q, K, V, scale, logits=logits, evicted=ev.copy())
+    b = unit_step(pol, T, "bf16", q, K, V, scale, logits=logits, evicted=ev.copy(), ed=True)
+    assert np.array_equal(a.sel, b.sel) and np.array_equal(a.evicted, b.evicted)
+    tok = attention.selected_tokens(b.sel, g, T)
+    bias = np.concatenate([np.full(min((j + 1) * g, T) - j * g, float(logits[j])) for j in b.sel])
+    assert np.allclose(b.out_exact, pins._dense_additive(q, K, V, tok, bias, scale),
+                       rtol=1e-12, atol=1e-12)
+    assert not np.allclose(a.out_exact, b.out_exact)
+
+
 def test_delta():
     pins.check_delta(delta.selection_delta, delta.locality)
 
