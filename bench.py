@@ -34,18 +34,20 @@ def log(msg: str) -> None:
     print(msg, file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(w, max_sel, sel_idx, sel_cnt):
+def algorithmic_bytes(w, max_sel, sel_idx, sel_cnt, ed=False):
     """The method's own HBM traffic for one step (decode partials and scores excluded).
 
     Per unit: KV = 2 d e N (N = valid tokens of the selected blocks); summaries read by
     scoring = n_full d e (retrieval / NOSA units); newest-block summary build = g d e read
-    + d e write; NOSA logits n_full * 4 and mask words read + written.  Shared: q read by
+    + d e write; NOSA logits n_full * 4 and mask words read + written (with the eviction
+    term in attention, also 4 bytes per selected block of a NOSA unit).  Shared: q read by
     select and decode, out written, lse written, selection indices written by select,
     read by decode, read twice and written twice (padded) by the delta.
     """
     import numpy as np
     e, d = w.elem_bytes, w.head_dim
-    parts = dict(kv=0, summaries=0, build=0, logits_mask=0, q=0, out=0, lse=0, indices=0)
+    parts = dict(kv=0, summaries=0, build=0, logits_mask=0, q=0, out=0, lse=0, indices=0,
+                 ed_logits=0)
     n_q = w.batch * w.num_q_heads
     tot_cnt = 0
     for u in range(w.num_units):
@@ -64,16 +66,19 @@ def algorithmic_bytes(w, max_sel, sel_idx, sel_cnt):
             parts["build"] += g * d * e + d * e
         if p.mode == 2:
             parts["logits_mask"] += n_full * 4 + 2 * 4 * (-(-n_full // 32))
+            if ed:
+                parts["ed_logits"] += cnt * 4
     parts["q"] = 2 * n_q * d * e
     parts["out"] = n_q * d * e
     parts["lse"] = n_q * 4
     parts["indices"] = (w.num_units * max_sel * 4) + tot_cnt * 4 + 2 * tot_cnt * 4 \
         + 2 * w.num_units * max_sel * 4
     total = sum(parts.values())
-    decode = parts["kv"] + n_q * d * e + parts["out"] + parts["lse"] + tot_cnt * 4
+    decode = (parts["kv"] + n_q * d * e + parts["out"] + parts["lse"] + tot_cnt * 4
+              + parts["ed_logits"])
     # fx_select + fx_sparse_decode alone: no summary build, no delta.
     sel_dec = (parts["kv"] + parts["summaries"] + parts["logits_mask"] + parts["q"] + parts["out"]
-               + parts["lse"] + w.num_units * max_sel * 4 + tot_cnt * 4)
+               + parts["lse"] + w.num_units * max_sel * 4 + tot_cnt * 4 + parts["ed_logits"])
     return total, decode, sel_dec, parts
 
 
@@ -102,7 +107,7 @@ def measured_traffic(workload: str):
         return None
 
 
-def cpu_baseline(w, inp, seconds: float, seed: int = 0):
+def cpu_baseline(w, inp, seconds: float, seed: int = 0, ed: bool = False):
     """Time the oracle on a bounded sample of this workload's units, one step each."""
     import numpy as np
     from threadpoolctl import threadpool_limits
@@ -129,7 +134,7 @@ def cpu_baseline(w, inp, seconds: float, seed: int = 0):
             t0 = time.perf_counter()
             if n_full >= 1:
                 block_summaries(K[(n_full - 1) * g:n_full * g], g, p.sub_block, w.dtype)
-            r = unit_step(p, T, w.dtype, q_rows, K, V, scale, logits=logits, summaries=summ)
+            r = unit_step(p, T, w.dtype, q_rows, K, V, scale, logits=logits, summaries=summ, ed=ed)
             selection_delta(np.zeros(0, np.int64), r.sel)
             spent += time.perf_counter() - t0
             N = int(np.minimum(g, T - r.sel * g).clip(min=0).sum())
@@ -160,6 +165,9 @@ def main() -> int:
     ap.add_argument("--no-flush", action="store_true",
                     help="skip the 1 GiB overwrite between steps (outside the timed events) "
                          "that keeps the 256 MB Infinity Cache from holding the previous step")
+    ap.add_argument("--ed", action="store_true",
+                    help="attention adds each NOSA block's eviction logit to its tokens' logits "
+                         "(fx_sparse_decode_ed)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-reference", action="store_true",
@@ -214,8 +222,12 @@ def main() -> int:
         fx.fx_select(plan, q, A.summaries, logits, mask, inp.seq_lens, cur.sel_idx, cur.sel_cnt,
                      A.workspace)
         ev_d0[i].record()
-        fx.fx_sparse_decode(plan, q, inp.K, inp.V, inp.seq_lens, cur.sel_idx, cur.sel_cnt, scale,
-                            A.out, A.lse, A.workspace)
+        if args.ed:
+            fx.fx_sparse_decode_ed(plan, q, inp.K, inp.V, inp.seq_lens, cur.sel_idx, cur.sel_cnt,
+                                   logits, scale, A.out, A.lse, A.workspace)
+        else:
+            fx.fx_sparse_decode(plan, q, inp.K, inp.V, inp.seq_lens, cur.sel_idx, cur.sel_cnt,
+                                scale, A.out, A.lse, A.workspace)
         ev_d1[i].record()
         fx.fx_selection_delta(plan, prev.sel_idx, prev.sel_cnt, cur.sel_idx, cur.sel_cnt,
                               A.added, A.added_cnt, A.removed, A.removed_cnt)
@@ -309,7 +321,8 @@ def main() -> int:
     sel_idx = prev.sel_idx.cpu().numpy()      # the last step's selection
     sel_cnt = prev.sel_cnt.cpu().numpy()
     w_last = w.replace(seq_lens=tuple(lens))      # the lengths of the last timed step
-    total_b, dec_b, sd_b, parts = algorithmic_bytes(w_last, plan.max_selected, sel_idx, sel_cnt)
+    total_b, dec_b, sd_b, parts = algorithmic_bytes(w_last, plan.max_selected, sel_idx, sel_cnt,
+                                                    ed=args.ed)
     value = total_b / (ms_per_step * 1e-3) / 1e9
     achieved = dec_b / (dec_avg * 1e-3) / 1e9
     sd_med = float(np.median(phases["select_decode"]))
@@ -328,7 +341,7 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] timing the CPU oracle on a sample (~{args.cpu_seconds:.0f} s)")
-        cpu = cpu_baseline(w, inp, args.cpu_seconds)
+        cpu = cpu_baseline(w, inp, args.cpu_seconds, ed=args.ed)
         log(f"[bench] oracle: {cpu['value']:.4f} GB/s ({cpu['sample']})")
 
     shapes = {
@@ -338,6 +351,7 @@ def main() -> int:
         "blocks": sorted({p.block for p in w.policies}), "split_tokens": plan.split_tokens,
         "cache_flush_between_steps": not args.no_flush,
         "decode_loop_growth": bool(args.grow),
+        "eviction_logit_in_attention": bool(args.ed),
     }
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
@@ -348,10 +362,12 @@ def main() -> int:
         "data": "synthetic (seeded; shapes and value distributions of the workload definition)",
         "config": shapes,
         "alg_bytes_per_step": int(total_b),
-        "roofline": {"bound": "hbm", "kernel": "fx_sparse_decode (k_decode + k_combine)",
+        "roofline": {"bound": "hbm",
+                     "kernel": ("fx_sparse_decode_ed" if args.ed else "fx_sparse_decode")
+                     + " (k_decode + k_combine)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(w.name),
+                     "traffic": None if args.ed else measured_traffic(w.name),
                      "alg_bytes_per_launch": int(dec_b), "avg_launch_us": round(dec_avg * 1e3, 2),
                      "k_decode_sha256_16": decode_source_hash()},
         "cpu_baseline": cpu,

@@ -22,7 +22,7 @@ __all__ = [
     "FX_ERR_SEQ_LEN", "FX_ERR_SEL_INDEX", "FX_ERR_SEL_COUNT", "FX_ERR_NONFINITE",
     "FxError", "Plan", "library_path", "load_library",
     "fx_plan_create", "fx_plan_destroy", "fx_build_summaries", "fx_select",
-    "fx_sparse_decode", "fx_selection_delta", "fx_read_error", "fx_status_string",
+    "fx_sparse_decode", "fx_sparse_decode_ed", "fx_selection_delta", "fx_read_error", "fx_status_string",
     "fx_stream_read",
     "StepBuffers", "allocate_step_buffers",
 ]
@@ -89,6 +89,8 @@ def load_library(path: Optional[str] = None):
         "fx_select": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
         "fx_sparse_decode": (_I32, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P, _P,
                                     ctypes.c_size_t, _P]),
+        "fx_sparse_decode_ed": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
+                                       _P, ctypes.c_size_t, _P]),
         "fx_selection_delta": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
         "fx_stream_read_sink_words": (ctypes.c_size_t, [ctypes.c_size_t]),
         "fx_stream_read": (_I32, [_P, ctypes.c_size_t, _P, _P]),
@@ -250,6 +252,25 @@ def fx_sparse_decode(plan: Plan, q: torch.Tensor, K: torch.Tensor, V: torch.Tens
         _ptr(sel_idx, "sel_idx", torch.int32, plan.units * plan.max_selected),
         _ptr(sel_cnt, "sel_cnt", torch.int32, plan.units), float(softmax_scale),
         _ptr(out, "out", dt, nq * plan.head_dim), _ptr(lse, "lse", torch.float32, nq, optional=True),
+        _ptr(workspace, "workspace", torch.uint8, plan.workspace_bytes), workspace.numel(),
+        _stream(stream)))
+
+
+def fx_sparse_decode_ed(plan: Plan, q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
+                        seq_lens: torch.Tensor, sel_idx: torch.Tensor, sel_cnt: torch.Tensor,
+                        evict_logits: Optional[torch.Tensor], softmax_scale: float,
+                        out: torch.Tensor, lse: Optional[torch.Tensor], workspace: torch.Tensor,
+                        stream=None) -> None:
+    dt = plan.torch_dtype
+    nq = plan.batch * plan.num_q_heads
+    _check("fx_sparse_decode_ed", load_library().fx_sparse_decode_ed(
+        plan.handle, _ptr(q, "q", dt, nq * plan.head_dim), _ptr(K, "K", dt, _kv_numel(plan)),
+        _ptr(V, "V", dt, _kv_numel(plan)), _ptr(seq_lens, "seq_lens", torch.int32, plan.batch),
+        _ptr(sel_idx, "sel_idx", torch.int32, plan.units * plan.max_selected),
+        _ptr(sel_cnt, "sel_cnt", torch.int32, plan.units),
+        _ptr(evict_logits, "evict_logits", torch.float32, plan.logits_bytes // 4, optional=True),
+        float(softmax_scale), _ptr(out, "out", dt, nq * plan.head_dim),
+        _ptr(lse, "lse", torch.float32, nq, optional=True),
         _ptr(workspace, "workspace", torch.uint8, plan.workspace_bytes), workspace.numel(),
         _stream(stream)))
 

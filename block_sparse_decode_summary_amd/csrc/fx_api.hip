@@ -140,6 +140,7 @@ fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_pl
           std::max<int32_t>(p->max_scored_n_full_cap, (int32_t)(desc->t_cap / q.block));
     }
     if (q.mode == FX_NOSA && q.k_evict > 0) p->needs_logits = true;
+    if (q.mode == FX_NOSA) p->any_nosa = true;
   }
   if (moff > INT32_MAX || max_sel > INT32_MAX / 2) {
     delete p;
@@ -157,8 +158,9 @@ fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_pl
     return FX_E_UNSUPPORTED;
   }
   p->split = desc->split_tokens != 0 ? desc->split_tokens : fx::kAutoSplit;
-  p->decode_grid = fx::decode_grid(p);
-  if (p->decode_grid <= 0) {
+  p->decode_grid = fx::decode_grid(p, false);
+  p->decode_grid_ed = std::min(fx::decode_grid(p, true), p->decode_grid);
+  if (p->decode_grid <= 0 || p->decode_grid_ed <= 0) {
     delete p;
     return FX_E_HIP;
   }
@@ -317,10 +319,12 @@ fx_status fx_select(fx_plan_t p, const void* q, const void* summaries, const flo
   }
 }
 
-fx_status fx_sparse_decode(fx_plan_t p, const void* q, const void* K, const void* V,
-                           const int32_t* seq_lens, const int32_t* sel_idx,
-                           const int32_t* sel_cnt, float softmax_scale, void* out, float* lse,
-                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+fx_status sparse_decode(fx_plan_t p, const void* q, const void* K, const void* V,
+                        const int32_t* seq_lens, const int32_t* sel_idx, const int32_t* sel_cnt,
+                        const float* logits, float softmax_scale, void* out, float* lse,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
   if (!p || !req(q, 16) || !req(K, 16) || !req(V, 16) || !req(seq_lens, 4) ||
       !req(sel_idx, 4) || !req(sel_cnt, 4) || !req(out, 16) || !opt(lse, 4) ||
       !req(workspace, 16))
@@ -329,13 +333,36 @@ fx_status fx_sparse_decode(fx_plan_t p, const void* q, const void* K, const void
   if (workspace_bytes < p->ws_total) return FX_E_WORKSPACE;
   try {
     char* ws = static_cast<char*>(workspace);
-    return hip_status(fx::launch_decode(p, q, K, V, seq_lens, sel_idx, sel_cnt, softmax_scale, out,
-                                        lse, reinterpret_cast<float*>(ws + p->ws_part_o_off),
+    return hip_status(fx::launch_decode(p, q, K, V, seq_lens, sel_idx, sel_cnt, logits,
+                                        softmax_scale, out, lse,
+                                        reinterpret_cast<float*>(ws + p->ws_part_o_off),
                                         reinterpret_cast<float*>(ws + p->ws_part_ml_off),
                                         reinterpret_cast<int32_t*>(ws + p->ws_seg_off), stream));
   } catch (...) {
     return FX_E_HIP;
   }
+}
+
+}  // namespace
+
+fx_status fx_sparse_decode(fx_plan_t p, const void* q, const void* K, const void* V,
+                           const int32_t* seq_lens, const int32_t* sel_idx,
+                           const int32_t* sel_cnt, float softmax_scale, void* out, float* lse,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return sparse_decode(p, q, K, V, seq_lens, sel_idx, sel_cnt, nullptr, softmax_scale, out, lse,
+                       workspace, workspace_bytes, stream);
+}
+
+fx_status fx_sparse_decode_ed(fx_plan_t p, const void* q, const void* K, const void* V,
+                              const int32_t* seq_lens, const int32_t* sel_idx,
+                              const int32_t* sel_cnt, const float* evict_logits,
+                              float softmax_scale, void* out, float* lse, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+  if (!p || !opt(evict_logits, 4) || (p->any_nosa && !evict_logits)) return FX_E_INVALID;
+  // Without NOSA units there is no eviction term: plain attention.
+  return sparse_decode(p, q, K, V, seq_lens, sel_idx, sel_cnt,
+                       p->any_nosa ? evict_logits : nullptr, softmax_scale, out, lse, workspace,
+                       workspace_bytes, stream);
 }
 
 fx_status fx_selection_delta(fx_plan_t p, const int32_t* prev_idx, const int32_t* prev_cnt,

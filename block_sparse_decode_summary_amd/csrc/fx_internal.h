@@ -66,8 +66,10 @@ struct fx_plan {
   int32_t max_n_full_cap = 0;    // max over units of t_cap / g
   int32_t split = 0;             // minimum decode segment in tokens (power of two)
   int32_t decode_grid = 0;       // decode workgroups = decode segments
+  int32_t decode_grid_ed = 0;    // the same for fx_sparse_decode_ed (<= decode_grid)
   bool any_scored = false;       // some unit is retrieval or NOSA
   bool needs_logits = false;     // some NOSA unit has k_evict > 0
+  bool any_nosa = false;         // some unit is NOSA
 
   // workspace layout (byte offsets)
   size_t ws_scores_off = 0;      // float [total_blocks]
@@ -92,12 +94,17 @@ hipError_t launch_topk(const fx_plan* p, const float* scores, const float* logit
                        int32_t* sel_cnt, uint32_t* ws_keys, uint32_t* ws_bits,
                        hipStream_t stream);
 bool topk_in_registers(const fx_plan* p);   // else keys and bitmaps use the workspace
+// logits == nullptr: plain attention; else each NOSA unit's token of block j also adds
+// logits[block_off + j] to its attention logit.
 hipError_t launch_decode(const fx_plan* p, const void* q, const void* K, const void* V,
                          const int32_t* seq_lens, const int32_t* sel_idx,
-                         const int32_t* sel_cnt, float softmax_scale, void* out, float* lse,
-                         float* part_o, float* part_ml, int32_t* seg_rec, hipStream_t stream);
-int decode_grid(const fx_plan* p);
-hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);   // resident decode workgroups on the current device (0: error)
+                         const int32_t* sel_cnt, const float* logits, float softmax_scale,
+                         void* out, float* lse, float* part_o, float* part_ml, int32_t* seg_rec,
+                         hipStream_t stream);
+// Resident decode workgroups on the current device (0: error); ed: the instantiation
+// with the eviction-logit term.
+int decode_grid(const fx_plan* p, bool ed);
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
 hipError_t launch_delta(const fx_plan* p, const int32_t* prev_idx, const int32_t* prev_cnt,
                         const int32_t* cur_idx, const int32_t* cur_cnt, int32_t* added,
                         int32_t* added_cnt, int32_t* removed, int32_t* removed_cnt,

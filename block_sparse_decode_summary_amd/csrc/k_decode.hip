@@ -9,6 +9,9 @@
 // Per unit (sequence b, kv head h) and query row q of its group:
 //   s_t = scale * (q . K_t) over the valid tokens t of the selected blocks,
 //   out = sum_t e^{s_t - m} V_t / l,  l = sum_t e^{s_t - m},  lse = m + ln l.
+// With exp-delayed eviction scores (the ED instantiation), a NOSA unit's token t of
+// block j has s_t = scale * (q . K_t) + b_j, b_j the block's raw eviction logit: its
+// exponential is formed only inside the softmax.  Other units have no eviction head.
 // The selected tokens of a unit are numbered i = 0 .. N-1 in ascending order; because
 // only the last block of a unit can be partial and selections are ascending, token i
 // lives in selected block i / g at offset i % g.
@@ -157,9 +160,10 @@ __device__ __forceinline__ UnitTokens unit_tokens(const UnitInfo* units, const i
   return {T, N};
 }
 
-template <typename E, int D, int G>
+template <typename E, int D, int G, bool ED>
 struct DecodeLds {
   int blk[kMaxSplit + 1];          // selected block indices of the current token run
+  float bias[ED ? kMaxSplit + 1 : 1];   // their eviction logits times log2(e) (ED only)
   float o[NWAVES][G][D];
   float m[NWAVES][G];
   float l[NWAVES][G];
@@ -197,11 +201,12 @@ __device__ __forceinline__ void write_empty_unit(E* out, float* lse, int u, int 
   }
 }
 
-template <typename E, int D, int G, int U>
+template <typename E, int D, int G, int U, bool ED>
 __global__ __launch_bounds__(NT) void k_decode(
     const UnitInfo* __restrict__ units, const E* __restrict__ q, const E* __restrict__ K,
     const E* __restrict__ V, const int32_t* __restrict__ seq_lens,
-    const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ sel_cnt, float scale_log2,
+    const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ sel_cnt,
+    const float* __restrict__ logits, float scale_log2,
     E* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
     float2* __restrict__ part_ml, int2* __restrict__ seg_rec, uint32_t* __restrict__ err,
     int Hkv, int t_cap, int max_sel, int n_units, int split) {
@@ -210,7 +215,7 @@ __global__ __launch_bounds__(NT) void k_decode(
   constexpr int TPW = 64 / LPT;       // tokens per wave instruction
   constexpr int STEP = TPW * U;       // tokens per wave per step
   static_assert(LPT >= 4 && LPT <= 32 && 64 % LPT == 0, "lane layout");
-  __shared__ DecodeLds<E, D, G> L;
+  __shared__ DecodeLds<E, D, G, ED> L;
   const int P = gridDim.x, seg = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
@@ -289,6 +294,7 @@ __global__ __launch_bounds__(NT) void k_decode(
     const int T = ut.T;
     const UnitInfo ui = units[u];
     const int g = ui.g, log2g = ui.log2g;
+    const bool biased = ED && ui.mode == FX_NOSA;
     const int b = u / Hkv, h = u % Hkv;
     const int32_t* sel = sel_idx + (size_t)u * max_sel;
     const int a = cur - Pu, e = min(s1, Pu + N) - Pu;   // piece [a, e) of the unit's tokens
@@ -327,6 +333,14 @@ __global__ __launch_bounds__(NT) void k_decode(
         const bool ok = jb >= 0 && (int64_t)jb * g < T && (p0 + i == 0 || sel[p0 + i - 1] < jb);
         if (!ok) atomicOr(err, (uint32_t)FX_ERR_SEL_INDEX);
         L.blk[i] = ok ? jb : -1;
+        if constexpr (ED) {
+          float bj = biased && ok ? logits[ui.block_off + jb] : 0.0f;
+          if (!__builtin_isfinite(bj)) {
+            atomicOr(err, (uint32_t)FX_ERR_NONFINITE);
+            bj = 0.0f;
+          }
+          L.bias[i] = bj * kLog2e;
+        }
       }
       __syncthreads();
 
@@ -335,13 +349,15 @@ __global__ __launch_bounds__(NT) void k_decode(
       const int w0 = c0 + wave * per_wave;
       const int w1 = min(c1, w0 + per_wave);
 
-      auto load_step = [&](int base, uint4* kr, uint4* vr, bool* ok) {
+      auto load_step = [&](int base, uint4* kr, uint4* vr, bool* ok, float* bs) {
         // Block indices first (independent LDS reads), then all 2U buffer loads.
         int jb[U];
 #pragma unroll
         for (int uu = 0; uu < U; ++uu) {
           const int i = base + uu * TPW + lg;
-          jb[uu] = L.blk[max(0, min((i >> log2g) - p0, np - 1))];
+          const int slot = max(0, min((i >> log2g) - p0, np - 1));
+          jb[uu] = L.blk[slot];
+          if constexpr (ED) bs[uu] = L.bias[slot];
         }
 #pragma unroll
         for (int uu = 0; uu < U; ++uu) {
@@ -354,7 +370,7 @@ __global__ __launch_bounds__(NT) void k_decode(
         }
       };
 
-      auto compute_step = [&](const uint4* kr, const uint4* vr, const bool* ok) {
+      auto compute_step = [&](const uint4* kr, const uint4* vr, const bool* ok, const float* bs) {
         float sc[U][G];
 #pragma unroll
         for (int uu = 0; uu < U; ++uu)
@@ -364,7 +380,8 @@ __global__ __launch_bounds__(NT) void k_decode(
         for (int uu = 0; uu < U; ++uu)
 #pragma unroll
           for (int gg = 0; gg < G; ++gg) {
-            const float t = group_sum<LPT>(sc[uu][gg]) * scale_log2;
+            float t = group_sum<LPT>(sc[uu][gg]) * scale_log2;
+            if constexpr (ED) t += bs[uu];
             sc[uu][gg] = ok[uu] ? t : -__builtin_inff();
           }
         // Rescale o and l only when some running max of the wave grew (a wave-uniform
@@ -421,13 +438,14 @@ __global__ __launch_bounds__(NT) void k_decode(
       // every path and each compute waits only for its own step's loads.
       uint4 kA[U], vA[U], kB[U], vB[U];
       bool okA[U], okB[U];
+      float bA[U], bB[U];   // ED only
       if (w0 < w1) {
-        load_step(w0, kA, vA, okA);
+        load_step(w0, kA, vA, okA, bA);
         for (int base = w0; base < w1; base += 2 * STEP) {
-          load_step(base + STEP, kB, vB, okB);
-          compute_step(kA, vA, okA);
-          load_step(base + 2 * STEP, kA, vA, okA);
-          if (base + STEP < w1) compute_step(kB, vB, okB);
+          load_step(base + STEP, kB, vB, okB, bB);
+          compute_step(kA, vA, okA, bA);
+          load_step(base + 2 * STEP, kA, vA, okA, bA);
+          if (base + STEP < w1) compute_step(kB, vB, okB, bB);
         }
       }
     }
@@ -565,15 +583,22 @@ constexpr int kU = 4;   // tokens per lane group per step
 template <typename E, int D, int G>
 hipError_t launch_t(const fx_plan* p, const void* q, const void* K, const void* V,
                     const int32_t* seq_lens, const int32_t* sel_idx, const int32_t* sel_cnt,
-                    float softmax_scale, void* out, float* lse, float* part_o, float* part_ml,
-                    int2* seg_rec, hipStream_t stream) {
+                    const float* logits, float softmax_scale, void* out, float* lse,
+                    float* part_o, float* part_ml, int2* seg_rec, hipStream_t stream) {
   const int Hkv = p->desc.num_kv_heads, t_cap = p->desc.t_cap;
-  const dim3 grid((unsigned)p->decode_grid);
-  k_decode<E, D, G, kU><<<grid, NT, 0, stream>>>(
-      p->d_units, static_cast<const E*>(q), static_cast<const E*>(K), static_cast<const E*>(V),
-      seq_lens, sel_idx, sel_cnt, softmax_scale * kLog2e, static_cast<E*>(out), lse, part_o,
-      reinterpret_cast<float2*>(part_ml), seg_rec, p->d_error, Hkv, t_cap, p->max_sel, p->units,
-      p->split);
+  const dim3 grid((unsigned)(logits ? p->decode_grid_ed : p->decode_grid));
+  // Every argument but the logits is the same for both instantiations.
+  auto args = [&](auto kernel) {
+    kernel<<<grid, NT, 0, stream>>>(
+        p->d_units, static_cast<const E*>(q), static_cast<const E*>(K),
+        static_cast<const E*>(V), seq_lens, sel_idx, sel_cnt, logits, softmax_scale * kLog2e,
+        static_cast<E*>(out), lse, part_o, reinterpret_cast<float2*>(part_ml), seg_rec,
+        p->d_error, Hkv, t_cap, p->max_sel, p->units, p->split);
+  };
+  if (logits)
+    args(k_decode<E, D, G, kU, true>);
+  else
+    args(k_decode<E, D, G, kU, false>);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // One thread per output (query row, column).
@@ -583,13 +608,14 @@ hipError_t launch_t(const fx_plan* p, const void* q, const void* K, const void* 
   return hipGetLastError();
 }
 
-template <typename E, int D, int G>
+template <typename E, int D, int G, bool ED>
 int grid_t() {
   int per_cu = 0, cus = 0, dev = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, reinterpret_cast<const void*>(&k_decode<E, D, G, kU>), NT, 0) != hipSuccess)
+          &per_cu, reinterpret_cast<const void*>(&k_decode<E, D, G, kU, ED>), NT, 0) !=
+          hipSuccess)
     return 0;
   return per_cu * cus;
 }
@@ -621,14 +647,16 @@ auto with_shape(const fx_plan* p, F&& f) {
 }
 
 struct GridFn {
+  bool ed;
   template <typename E, int D, int G>
-  int operator()() const { return grid_t<E, D, G>(); }
+  int operator()() const { return ed ? grid_t<E, D, G, true>() : grid_t<E, D, G, false>(); }
 };
 
 struct LaunchFn {
   const fx_plan* p;
   const void *q, *K, *V;
   const int32_t *seq_lens, *sel_idx, *sel_cnt;
+  const float* logits;
   float softmax_scale;
   void* out;
   float *lse, *part_o, *part_ml;
@@ -636,22 +664,23 @@ struct LaunchFn {
   hipStream_t stream;
   template <typename E, int D, int G>
   hipError_t operator()() const {
-    return launch_t<E, D, G>(p, q, K, V, seq_lens, sel_idx, sel_cnt, softmax_scale, out, lse,
-                             part_o, part_ml, seg_rec, stream);
+    return launch_t<E, D, G>(p, q, K, V, seq_lens, sel_idx, sel_cnt, logits, softmax_scale, out,
+                             lse, part_o, part_ml, seg_rec, stream);
   }
 };
 
 }  // namespace
 
-int decode_grid(const fx_plan* p) { return with_shape(p, GridFn{}); }
+int decode_grid(const fx_plan* p, bool ed) { return with_shape(p, GridFn{ed}); }
 
 hipError_t launch_decode(const fx_plan* p, const void* q, const void* K, const void* V,
                          const int32_t* seq_lens, const int32_t* sel_idx, const int32_t* sel_cnt,
-                         float softmax_scale, void* out, float* lse, float* part_o,
-                         float* part_ml, int32_t* seg_rec, hipStream_t stream) {
+                         const float* logits, float softmax_scale, void* out, float* lse,
+                         float* part_o, float* part_ml, int32_t* seg_rec, hipStream_t stream) {
   if (p->G < 1 || p->G > kMaxGroup) return hipErrorInvalidValue;
-  return with_shape(p, LaunchFn{p, q, K, V, seq_lens, sel_idx, sel_cnt, softmax_scale, out, lse,
-                                part_o, part_ml, reinterpret_cast<int2*>(seg_rec), stream});
+  return with_shape(p, LaunchFn{p, q, K, V, seq_lens, sel_idx, sel_cnt, logits, softmax_scale,
+                                out, lse, part_o, part_ml, reinterpret_cast<int2*>(seg_rec),
+                                stream});
 }
 
 }  // namespace fx

@@ -9,6 +9,8 @@
  *                       block selection (streaming / retrieval top-k / NOSA)
  *   fx_sparse_decode    flash-decoding over the selected blocks only, split evenly
  *                       across the GPU
+ *   fx_sparse_decode_ed the same with each NOSA block's eviction logit added to its
+ *                       tokens' attention logits (exp-delayed eviction scores)
  *   fx_selection_delta  blocks added to / removed from the previous selection
  *
  * Sources, cited by page title and section:
@@ -109,7 +111,8 @@ enum {
   FX_ERR_SEQ_LEN = 1u << 0,        /* a seq_len was outside [0, t_cap]; clamped */
   FX_ERR_SEL_INDEX = 1u << 1,      /* a selection entry was outside [0, n_tot) or not ascending; skipped */
   FX_ERR_SEL_COUNT = 1u << 2,      /* a sel_cnt was outside [0, max_sel]; clamped */
-  FX_ERR_NONFINITE = 1u << 3       /* a non-finite score or eviction logit; ranked lowest */
+  FX_ERR_NONFINITE = 1u << 3       /* a non-finite score or eviction logit; ranked lowest
+                                      (fx_sparse_decode_ed: counted as 0) */
 };
 
 typedef struct {
@@ -251,6 +254,24 @@ fx_status fx_sparse_decode(fx_plan_t plan, const void* q, const void* K, const v
                            const int32_t* sel_cnt, float softmax_scale, void* out,
                            float* lse, void* workspace, size_t workspace_bytes,
                            hipStream_t stream);
+
+/* [NOSA-DE] Methodik §1, "ED-DMA": the eviction head's exponential is taken only in the
+ * attention phase; selection ranks the values before it.  The page gives no formula;
+ * this call reads it as an additive pre-softmax term.
+ * As fx_sparse_decode, except that for every NOSA unit u each valid token t of a
+ * selected block j has
+ *     s_t = softmax_scale * (q . K_t) + b_j,   b_j = evict_logits[block_off(u) + j],
+ * so e^{b_j} multiplies the block's weights inside the softmax and is never formed on
+ * its own (lse includes the term).  Retrieval and streaming units have no eviction head
+ * and get exactly fx_sparse_decode's result.  evict_logits: float32 [total_blocks] in
+ * fx_select's layout (slots of blocks that are not selected are not read); required when
+ * the plan has a NOSA unit, else may be NULL.  A non-finite b_j counts as 0 and sets
+ * FX_ERR_NONFINITE.  Workspace and the other arguments as for fx_sparse_decode. */
+fx_status fx_sparse_decode_ed(fx_plan_t plan, const void* q, const void* K, const void* V,
+                              const int32_t* seq_lens, const int32_t* sel_idx,
+                              const int32_t* sel_cnt, const float* evict_logits,
+                              float softmax_scale, void* out, float* lse, void* workspace,
+                              size_t workspace_bytes, hipStream_t stream);
 
 /* [NOSA-DE] Methodik §2, bullet "Optimierte Speicherlayout" (set differences of
  * block selections drive block swapping); Methodik §1, "Lokalitätsgarantie".

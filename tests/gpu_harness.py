@@ -104,12 +104,13 @@ class GpuView:
         return bits.astype(bool)
 
 
-def oracle_unit(inp, u: int, q: torch.Tensor, evicted: Optional[np.ndarray] = None):
+def oracle_unit(inp, u: int, q: torch.Tensor, evicted: Optional[np.ndarray] = None,
+                ed: bool = False):
     w = inp.workload
     b, h = divmod(u, w.num_kv_heads)
     q_rows, K, V = unit_arrays(inp, b, h, q=q)
     return unit_step(w.policies[u], w.seq_lens[b], w.dtype, q_rows, K, V, softmax_scale(w),
-                     logits=unit_logits(inp, u), evicted=evicted)
+                     logits=unit_logits(inp, u), evicted=evicted, ed=ed)
 
 
 def assert_close(name: str, got: np.ndarray, ref: np.ndarray, rtol: float, atol: float) -> float:
