@@ -24,8 +24,9 @@ routines; none is "parity unpinned".
 
 Modules
   numerics   float64 -> bfloat16 / float32 rounding (round to nearest, ties to even)
-  pooling    two-stage block summaries (mean over sub-blocks, max over the block)
-  scoring    block scores against the GQA query group
+  pooling    two-stage block summaries (mean over sub-blocks, max over the block), or
+             the sub-block means alone for score-side pooling
+  scoring    block scores against the GQA query group (key-side or score-side pooling)
   selection  forced sets, top-k per kv head, NOSA eviction selection
   attention  attention over the selected tokens; split-K partial merge
   delta      selection set differences and locality

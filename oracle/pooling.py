@@ -6,7 +6,10 @@ inside each sub-block, followed by a max at block level.
 
 Readings taken where the page is silent:
 * The pooling acts on the key rows and the max is elementwise over the
-  sub-block mean vectors, giving one query-independent d-vector per full block.
+  sub-block mean vectors, giving one query-independent d-vector per full block
+  (block_summaries).  The other reading, the max taken over the scores of the
+  sub-block means, keeps every mean (sub_block_means) and leaves the max to
+  scoring.sub_block_scores.
 * Only full blocks get a summary; a partial last block has none.
 * Precision: the sub-block sums are formed in float64, where they are exact for
   the inputs used here (checked below, the function refuses otherwise); the
@@ -39,6 +42,18 @@ def _check_exact_sums(x: np.ndarray, p: int) -> None:
         raise ValueError("pooling: a float64 sub-block sum would be inexact for these inputs")
 
 
+def _exact_means(K: np.ndarray, block: int, sub_block: int, dtype: str) -> np.ndarray:
+    """m[j, u] = (sum of the sub_block rows of sub-block u of block j) / sub_block, exact,
+    float64 [n_full][block/sub_block][d]."""
+    if block % sub_block != 0:
+        raise ValueError("sub_block must divide block")
+    T, d = K.shape
+    n_full = T // block
+    x = K[: n_full * block].reshape(n_full, block // sub_block, sub_block, d)
+    _check_exact_sums(x, significant_bits(dtype))
+    return x.sum(axis=2) / sub_block
+
+
 def block_summaries(K: np.ndarray, block: int, sub_block: int, dtype: str) -> np.ndarray:
     """Summaries S[j] for the full blocks of one (sequence, kv head).
 
@@ -47,12 +62,14 @@ def block_summaries(K: np.ndarray, block: int, sub_block: int, dtype: str) -> np
         m[j, u] = (sum of the sub_block rows of sub-block u of block j) / sub_block
         S[j]    = round_once(elementwise max over u of m[j, u])
     """
-    if block % sub_block != 0:
-        raise ValueError("sub_block must divide block")
-    T, d = K.shape
-    n_full = T // block
-    x = K[: n_full * block].reshape(n_full, block // sub_block, sub_block, d)
-    _check_exact_sums(x, significant_bits(dtype))
-    means = x.sum(axis=2) / sub_block            # [n_full][block/sub_block][d], exact
-    pooled = means.max(axis=1)                   # [n_full][d]
-    return round_to_storage(pooled, dtype)
+    means = _exact_means(K, block, sub_block, dtype)
+    return round_to_storage(means.max(axis=1), dtype)
+
+
+def sub_block_means(K: np.ndarray, block: int, sub_block: int, dtype: str) -> np.ndarray:
+    """The first pooling stage alone, for score-side pooling (the block-level max is
+    then taken over scores, not over vectors; see scoring.sub_block_scores).
+
+    Returns float64 [T // block][block // sub_block][d]: every m[j, u] rounded once into
+    ``dtype`` (to nearest, ties to even)."""
+    return round_to_storage(_exact_means(K, block, sub_block, dtype), dtype)

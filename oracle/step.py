@@ -17,14 +17,15 @@ import numpy as np
 
 from .attention import attend, selected_tokens, token_bias
 from .numerics import round_to_storage
-from .pooling import block_summaries
-from .scoring import block_scores
+from .pooling import block_summaries, sub_block_means
+from .scoring import POOL_KEY, block_scores, sub_block_scores
 from .selection import MODE_NOSA, MODE_STREAMING, select_unit
 
 
 @dataclass
 class UnitResult:
-    summaries: np.ndarray           # float64 [n_full][d], representable in the storage dtype
+    summaries: np.ndarray           # float64 [n_full][d] ([n_full][r][d] under score-side
+                                    # pooling), representable in the storage dtype
     scores: Optional[np.ndarray]    # float32 [n_full] (None for streaming units)
     sel: np.ndarray                 # int64 ascending block indices
     evicted: Optional[np.ndarray]   # bool eviction state after the step (NOSA units)
@@ -36,14 +37,22 @@ class UnitResult:
 def unit_step(pol, T: int, dtype: str, q_rows: np.ndarray, K: np.ndarray, V: np.ndarray,
               scale: float, logits: Optional[np.ndarray] = None,
               evicted: Optional[np.ndarray] = None,
-              summaries: Optional[np.ndarray] = None, ed: bool = False) -> UnitResult:
+              summaries: Optional[np.ndarray] = None, ed: bool = False,
+              pooling: int = POOL_KEY) -> UnitResult:
     """q_rows float64 [G][d]; K, V float64 [T][d] (the unit's valid rows).
 
     ``ed``: a NOSA unit adds each selected block's eviction logit (``logits``, one per
     block slot of the unit) to its tokens' attention logits ([NOSA-DE] Methodik §1,
-    "ED-DMA"); other modes have no eviction head and are unaffected."""
-    S = block_summaries(K, pol.block, pol.sub_block, dtype) if summaries is None else summaries
-    scores = None if pol.mode == MODE_STREAMING else block_scores(q_rows, S)
+    "ED-DMA"); other modes have no eviction head and are unaffected.
+    ``pooling``: POOL_KEY pools the keys into one vector per block (summaries [n_full][d]);
+    POOL_SCORE_SUM / POOL_SCORE_MAX keep the sub-block means (summaries
+    [n_full][block/sub_block][d]) and take the block max over their scores."""
+    if pooling == POOL_KEY:
+        S = block_summaries(K, pol.block, pol.sub_block, dtype) if summaries is None else summaries
+        scores = None if pol.mode == MODE_STREAMING else block_scores(q_rows, S)
+    else:
+        S = sub_block_means(K, pol.block, pol.sub_block, dtype) if summaries is None else summaries
+        scores = None if pol.mode == MODE_STREAMING else sub_block_scores(q_rows, S, pooling)
     sel, ev = select_unit(pol, T, scores, logits, evicted)
     tok = selected_tokens(sel, pol.block, T)
     bias = None

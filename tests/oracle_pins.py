@@ -189,6 +189,92 @@ def check_scoring(block_scores):
     assert block_scores(q, S)[0] == np.float32(13.0)
 
 
+def check_sub_block_means(sub_block_means, block_summaries):
+    """Score-side pooling, first stage: every sub-block mean rounded once."""
+    rng = np.random.default_rng(23)
+    for dtype, to_storage in (("bf16", fraction_to_bf16), ("f32", fraction_to_f32)):
+        for g, s in ((16, 16), (32, 8), (64, 16), (16, 1), (8, 4)):
+            if dtype == "bf16":
+                K = random_bf16_values(rng, (3 * g + 5, 6), scale=3.0)
+            else:
+                K = rng.standard_normal((3 * g + 5, 6)).astype(np.float32).astype(np.float64)
+            M = sub_block_means(K, g, s, dtype)
+            assert M.shape == (3, g // s, 6)
+            for j in range(3):
+                for u in range(g // s):
+                    for c in range(6):
+                        exact = sum(Fraction(float(v)) for v in
+                                    K[j * g + u * s:j * g + (u + 1) * s, c]) / s
+                        assert Fraction(float(M[j, u, c])) == to_storage(exact), (dtype, g, s)
+            # rounding is monotone, so the max of the rounded means is the key-side summary.
+            assert np.array_equal(M.max(axis=1), block_summaries(K, g, s, dtype))
+    # the double-rounding trap, with bf16 rows (2, 2, 2^-6, 2^-27): the mean is
+    # 1 + 2^-8 + 2^-29, just above the tie between the bf16 neighbours 1 and 1 + 2^-7, and
+    # float32 would first round it onto that tie (then to the even neighbour, 1).
+    rows = np.array([[2.0], [2.0], [2.0 ** -6], [2.0 ** -27]])
+    M = sub_block_means(rows, 4, 4, "bf16")
+    exact = sum(Fraction(float(v)) for v in rows[:, 0]) / 4
+    assert Fraction(float(M[0, 0, 0])) == fraction_to_bf16(exact) == 1 + Fraction(1, 2 ** 7)
+
+
+def check_sub_block_scores(sub_block_scores, block_scores, POOL_SCORE_SUM, POOL_SCORE_MAX):
+    """Score-side pooling: block max over the sub-block means' scores; the group summed or
+    maxed."""
+    rng = np.random.default_rng(24)
+    # exact rational reference for both group aggregations.
+    for G, d, n, r in ((1, 8, 20, 4), (4, 16, 15, 2), (7, 32, 10, 4), (8, 128, 6, 16)):
+        q = random_bf16_values(rng, (G, d))
+        M = random_bf16_values(rng, (n, r, d), scale=2.0)
+        got_s = sub_block_scores(q, M, POOL_SCORE_SUM)
+        got_m = sub_block_scores(q, M, POOL_SCORE_MAX)
+        assert got_s.dtype == np.float32 and got_s.shape == (n,) and got_m.shape == (n,)
+        for j in range(n):
+            dots = [[sum(Fraction(float(q[g, c])) * Fraction(float(M[j, u, c])) for c in range(d))
+                     for u in range(r)] for g in range(G)]
+            want_s = max(sum(dots[g][u] for g in range(G)) for u in range(r))
+            want_m = max(max(row) for row in dots)
+            assert Fraction(float(got_s[j])) == fraction_to_f32(want_s), (G, d, r, j)
+            assert Fraction(float(got_m[j])) == fraction_to_f32(want_m), (G, d, r, j)
+    # one sub-block per block: the group-sum variant is key-side scoring bit for bit.
+    q = random_bf16_values(rng, (4, 64))
+    S = random_bf16_values(rng, (30, 64))
+    assert np.array_equal(sub_block_scores(q, S[:, None, :], POOL_SCORE_SUM), block_scores(q, S))
+    # G = 1: the two group aggregations agree.
+    M = random_bf16_values(rng, (12, 4, 32))
+    q1 = random_bf16_values(rng, (1, 32))
+    assert np.array_equal(sub_block_scores(q1, M, POOL_SCORE_SUM), sub_block_scores(q1, M, POOL_SCORE_MAX))
+    # hand example where the two pooling sides differ: q = (1, 1), sub-block means
+    # (1, 0) and (0, 1).  Key side: summary (1, 1), score 2.  Score side: max(1, 1) = 1.
+    qh = np.array([[1.0, 1.0]])
+    Mh = np.array([[[1.0, 0.0], [0.0, 1.0]]])
+    assert sub_block_scores(qh, Mh, POOL_SCORE_SUM)[0] == np.float32(1.0)
+    assert block_scores(qh, Mh.max(axis=1))[0] == np.float32(2.0)
+    # group of two rows e_0 and 3 e_1 against means (2, 0) and (0, 1):
+    # sum agg: max(2, 3) = 3; max agg: max(max(2, 0), max(0, 3)) = 3; with means (2, 0)
+    # and (0, 0.5): sum agg max(2, 1.5) = 2, max agg max(2, 1.5) = 2; and with a third
+    # row -e_0 the sum agg drops to max(0, 1.5) = 1.5 while the max agg stays 2.
+    qg = np.array([[1.0, 0.0], [0.0, 3.0]])
+    assert sub_block_scores(qg, np.array([[[2.0, 0.0], [0.0, 1.0]]]), POOL_SCORE_SUM)[0] == 3.0
+    assert sub_block_scores(qg, np.array([[[2.0, 0.0], [0.0, 1.0]]]), POOL_SCORE_MAX)[0] == 3.0
+    q3 = np.array([[1.0, 0.0], [0.0, 3.0], [-1.0, 0.0]])
+    M3 = np.array([[[2.0, 0.0], [0.0, 0.5]]])
+    assert sub_block_scores(q3, M3, POOL_SCORE_SUM)[0] == np.float32(1.5)
+    assert sub_block_scores(q3, M3, POOL_SCORE_MAX)[0] == np.float32(2.0)
+    # invariances: permuting the sub-blocks of a block, or the rows of the group.
+    q = random_bf16_values(rng, (4, 16))
+    M = random_bf16_values(rng, (10, 8, 16))
+    for pool in (POOL_SCORE_SUM, POOL_SCORE_MAX):
+        base = sub_block_scores(q, M, pool)
+        assert np.array_equal(sub_block_scores(q, M[:, rng.permutation(8)], pool), base)
+        assert np.array_equal(sub_block_scores(q[rng.permutation(4)], M, pool), base)
+    # with a non-negative query the key-side score bounds the group-sum score from above.
+    qp = np.abs(random_bf16_values(rng, (4, 16)))
+    Mp = random_bf16_values(rng, (40, 4, 16))
+    assert np.all(block_scores(qp, Mp.max(axis=1)) >= sub_block_scores(qp, Mp, POOL_SCORE_SUM))
+    # empty block list.
+    assert sub_block_scores(q, np.zeros((0, 8, 16)), POOL_SCORE_MAX).shape == (0,)
+
+
 # ----------------------------------------------------------------------------------------
 # selection
 # ----------------------------------------------------------------------------------------

@@ -248,6 +248,66 @@ def test_select_mutants(mutant, check):
     assert _fails(check, mutant)
 
 
+# ---- score-side pooling ---------------------------------------------------------------
+
+def _means_unrounded(K, g, s, dtype):          # the exact means, never rounded
+    return pooling._exact_means(K, g, s, dtype)
+
+
+def _means_via_f32(K, g, s, dtype):            # double rounding through float32
+    m = pooling._exact_means(K, g, s, dtype)
+    if dtype != "bf16":
+        return m
+    return numerics.round_f64_to_bf16(m.astype(np.float32).astype(np.float64))
+
+
+def _means_last_dropped(K, g, s, dtype):       # the last sub-block repeats the one before
+    m = pooling.sub_block_means(K, g, s, dtype)
+    if m.shape[1] > 1:
+        m[:, -1] = m[:, -2]
+    return m
+
+
+@pytest.mark.parametrize("mutant", [_means_unrounded, _means_via_f32, _means_last_dropped])
+def test_sub_block_means_mutants(mutant):
+    assert _fails(pins.check_sub_block_means, mutant, pooling.block_summaries)
+
+
+def _scores_key_side(q, M, pool):              # max over the means before scoring
+    return scoring.block_scores(q, np.asarray(M).max(axis=1))
+
+
+def _scores_mean_over_sub_blocks(q, M, pool):
+    M = np.asarray(M, dtype=np.float64)
+    if pool == scoring.POOL_SCORE_SUM:
+        return scoring._chain(scoring.group_query_sum(q), M).mean(axis=1).astype(np.float32)
+    return scoring.sub_block_scores(q, M, pool)
+
+
+def _scores_aggregations_swapped(q, M, pool):
+    other = scoring.POOL_SCORE_MAX if pool == scoring.POOL_SCORE_SUM else scoring.POOL_SCORE_SUM
+    return scoring.sub_block_scores(q, M, other)
+
+
+def _scores_max_agg_first_row_only(q, M, pool):
+    if pool == scoring.POOL_SCORE_MAX:
+        return scoring.sub_block_scores(np.asarray(q)[:1], M, scoring.POOL_SCORE_SUM)
+    return scoring.sub_block_scores(q, M, pool)
+
+
+def _scores_min_over_sub_blocks(q, M, pool):
+    return -scoring.sub_block_scores(q, -np.asarray(M, dtype=np.float64), pool) \
+        if pool == scoring.POOL_SCORE_SUM else scoring.sub_block_scores(q, M, pool)
+
+
+@pytest.mark.parametrize("mutant", [_scores_key_side, _scores_mean_over_sub_blocks,
+                                    _scores_aggregations_swapped, _scores_max_agg_first_row_only,
+                                    _scores_min_over_sub_blocks])
+def test_sub_block_scores_mutants(mutant):
+    assert _fails(pins.check_sub_block_scores, mutant, scoring.block_scores,
+                  scoring.POOL_SCORE_SUM, scoring.POOL_SCORE_MAX)
+
+
 # ---- attention ------------------------------------------------------------------------
 
 def _attend_no_scale(q, K, V, scale):

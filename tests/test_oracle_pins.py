@@ -29,6 +29,15 @@ def test_scoring():
     pins.check_scoring(scoring.block_scores)
 
 
+def test_sub_block_means():
+    pins.check_sub_block_means(pooling.sub_block_means, pooling.block_summaries)
+
+
+def test_sub_block_scores():
+    pins.check_sub_block_scores(scoring.sub_block_scores, scoring.block_scores,
+                                scoring.POOL_SCORE_SUM, scoring.POOL_SCORE_MAX)
+
+
 def test_forced_sets():
     pins.check_forced(selection.forced_blocks)
 
@@ -84,6 +93,29 @@ def test_unit_step_ed_biases_nosa_units_only():
     assert np.allclose(b.out_exact, pins._dense_additive(q, K, V, tok, bias, scale),
                        rtol=1e-12, atol=1e-12)
     assert not np.allclose(a.out_exact, b.out_exact)
+
+
+def test_unit_step_score_side_pooling():
+    """End to end: with sub_block = block the group-sum score-side pooling is key-side
+    pooling; with smaller sub-blocks the summaries keep every mean and the max moves to
+    the scores."""
+    rng = np.random.default_rng(25)
+    G, d, T = 4, 32, 700
+    q = pins.random_bf16_values(rng, (G, d))
+    K = pins.random_bf16_values(rng, (T, d))
+    V = pins.random_bf16_values(rng, (T, d))
+    scale = d ** -0.5
+    pol = pins.Pol(mode=0, block=32, sub_block=32, top_k=4, force_sink=1, force_last=1)
+    a = unit_step(pol, T, "bf16", q, K, V, scale)
+    b = unit_step(pol, T, "bf16", q, K, V, scale, pooling=scoring.POOL_SCORE_SUM)
+    assert np.array_equal(a.scores, b.scores) and np.array_equal(a.sel, b.sel)
+    assert np.array_equal(b.summaries[:, 0, :], a.summaries)
+    pol = pins.Pol(mode=0, block=32, sub_block=8, top_k=4)
+    for pool in (scoring.POOL_SCORE_SUM, scoring.POOL_SCORE_MAX):
+        r = unit_step(pol, T, "bf16", q, K, V, scale, pooling=pool)
+        assert r.summaries.shape == (T // 32, 4, d)
+        assert np.array_equal(r.scores, scoring.sub_block_scores(
+            q, pooling.sub_block_means(K, 32, 8, "bf16"), pool))
 
 
 def test_delta():
