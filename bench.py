@@ -38,8 +38,8 @@ def algorithmic_bytes(w, max_sel, sel_idx, sel_cnt, ed=False):
     """The method's own HBM traffic for one step (decode partials and scores excluded).
 
     Per unit: KV = 2 d e N (N = valid tokens of the selected blocks); summaries read by
-    scoring = n_full d e (retrieval / NOSA units); newest-block summary build = g d e read
-    + d e write; NOSA logits n_full * 4 and mask words read + written (with the eviction
+    scoring = n_full r d e (retrieval / NOSA units; r summary rows per block, 1 unless
+    pooling is score-side); newest-block summary build = g d e read + r d e write; NOSA logits n_full * 4 and mask words read + written (with the eviction
     term in attention, also 4 bytes per selected block of a NOSA unit).  Shared: q read by
     select and decode, out written, lse written, selection indices written by select,
     read by decode, read twice and written twice (padded) by the delta.
@@ -55,15 +55,16 @@ def algorithmic_bytes(w, max_sel, sel_idx, sel_cnt, ed=False):
         p = w.policies[u]
         T, g = w.seq_lens[b], p.block
         n_full = T // g
+        r = w.summary_rows_per_block(u)
         cnt = int(sel_cnt[u])
         tot_cnt += cnt
         sel = sel_idx[u, :cnt].astype(np.int64)
         N = int(np.minimum(g, T - sel * g).clip(min=0).sum())
         parts["kv"] += 2 * d * e * N
         if p.mode != 1:
-            parts["summaries"] += n_full * d * e
+            parts["summaries"] += n_full * r * d * e
         if n_full >= 1:
-            parts["build"] += g * d * e + d * e
+            parts["build"] += g * d * e + r * d * e
         if p.mode == 2:
             parts["logits_mask"] += n_full * 4 + 2 * 4 * (-(-n_full // 32))
             if ed:
@@ -113,7 +114,7 @@ def cpu_baseline(w, inp, seconds: float, seed: int = 0, ed: bool = False):
     from threadpoolctl import threadpool_limits
 
     from oracle.delta import selection_delta
-    from oracle.pooling import block_summaries
+    from oracle.pooling import block_summaries, sub_block_means
     from oracle.step import unit_step
     from workloads import unit_arrays
     from workloads.generate import unit_logits
@@ -129,17 +130,20 @@ def cpu_baseline(w, inp, seconds: float, seed: int = 0, ed: bool = False):
             T, g = w.seq_lens[b], p.block
             q_rows, K, V = unit_arrays(inp, b, h)
             logits = unit_logits(inp, int(u))
-            summ = block_summaries(K, p.block, p.sub_block, w.dtype)   # resident, not timed
+            pool_fn = block_summaries if w.pooling == 0 else sub_block_means
+            summ = pool_fn(K, p.block, p.sub_block, w.dtype)   # resident, not timed
             n_full = T // g
             t0 = time.perf_counter()
             if n_full >= 1:
-                block_summaries(K[(n_full - 1) * g:n_full * g], g, p.sub_block, w.dtype)
-            r = unit_step(p, T, w.dtype, q_rows, K, V, scale, logits=logits, summaries=summ, ed=ed)
+                pool_fn(K[(n_full - 1) * g:n_full * g], g, p.sub_block, w.dtype)
+            r = unit_step(p, T, w.dtype, q_rows, K, V, scale, logits=logits, summaries=summ, ed=ed,
+                          pooling=w.pooling)
             selection_delta(np.zeros(0, np.int64), r.sel)
             spent += time.perf_counter() - t0
             N = int(np.minimum(g, T - r.sel * g).clip(min=0).sum())
-            nbytes += 2 * d * e * N + (n_full * d * e if p.mode != 1 else 0) \
-                + (g * d * e + d * e if n_full else 0) + 3 * G * d * e + G * 4
+            rr = w.summary_rows_per_block(int(u))
+            nbytes += 2 * d * e * N + (n_full * rr * d * e if p.mode != 1 else 0) \
+                + (g * d * e + rr * d * e if n_full else 0) + 3 * G * d * e + G * 4
             done += 1
             if spent >= seconds:
                 break
@@ -168,6 +172,9 @@ def main() -> int:
     ap.add_argument("--ed", action="store_true",
                     help="attention adds each NOSA block's eviction logit to its tokens' logits "
                          "(fx_sparse_decode_ed)")
+    ap.add_argument("--pooling", choices=["key", "score_sum", "score_max"], default="key",
+                    help="where the block max of the two-stage pooling acts: over key vectors "
+                         "(one summary row per block) or over the scores of the sub-block means")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-reference", action="store_true",
@@ -189,6 +196,9 @@ def main() -> int:
     if args.workload not in WORKLOAD_NAMES:
         raise SystemExit(f"unknown workload {args.workload}; one of {WORKLOAD_NAMES}")
     w = get_workload(args.workload)
+    pooling = {"key": fx.FX_POOL_KEY, "score_sum": fx.FX_POOL_SCORE_SUM,
+               "score_max": fx.FX_POOL_SCORE_MAX}[args.pooling]
+    w = w.replace(pooling=pooling)
     if args.grow:
         w = w.replace(t_cap=w.t_cap + args.warmup + args.steps)
     dev = torch.device("cuda:0")
@@ -201,7 +211,7 @@ def main() -> int:
 
     dt = fx.FX_F32 if w.dtype == "f32" else fx.FX_BF16
     plan = fx.fx_plan_create(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.t_cap, dt,
-                             list(w.policies), args.split)
+                             list(w.policies), args.split, pooling)
     A = fx.allocate_step_buffers(plan, dev)
     Bsel = fx.allocate_step_buffers(plan, dev)     # second selection buffer for the delta
     scale = 1.0 / math.sqrt(w.head_dim)
@@ -352,6 +362,7 @@ def main() -> int:
         "cache_flush_between_steps": not args.no_flush,
         "decode_loop_growth": bool(args.grow),
         "eviction_logit_in_attention": bool(args.ed),
+        "pooling": args.pooling,
     }
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,

@@ -19,6 +19,7 @@ import torch
 
 __all__ = [
     "FX_F32", "FX_BF16", "FX_RETRIEVAL", "FX_STREAMING", "FX_NOSA",
+    "FX_POOL_KEY", "FX_POOL_SCORE_SUM", "FX_POOL_SCORE_MAX", "fx_unit_summary_offset",
     "FX_ERR_SEQ_LEN", "FX_ERR_SEL_INDEX", "FX_ERR_SEL_COUNT", "FX_ERR_NONFINITE",
     "FxError", "Plan", "library_path", "load_library",
     "fx_plan_create", "fx_plan_destroy", "fx_build_summaries", "fx_select",
@@ -30,6 +31,7 @@ __all__ = [
 FX_OK, FX_E_INVALID, FX_E_UNSUPPORTED, FX_E_WORKSPACE, FX_E_HIP = 0, 1, 2, 3, 4
 FX_F32, FX_BF16 = 0, 1
 FX_RETRIEVAL, FX_STREAMING, FX_NOSA = 0, 1, 2
+FX_POOL_KEY, FX_POOL_SCORE_SUM, FX_POOL_SCORE_MAX = 0, 1, 2
 FX_ERR_SEQ_LEN, FX_ERR_SEL_INDEX, FX_ERR_SEL_COUNT, FX_ERR_NONFINITE = 1, 2, 4, 8
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -49,7 +51,7 @@ class _PlanDesc(ctypes.Structure):
     _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("t_cap", ctypes.c_int32), ("dtype", ctypes.c_int32),
-                ("split_tokens", ctypes.c_int32)]
+                ("split_tokens", ctypes.c_int32), ("pooling", ctypes.c_int32)]
 
 
 class _HeadPolicy(ctypes.Structure):
@@ -82,6 +84,7 @@ def load_library(path: Optional[str] = None):
         "fx_workspace_bytes": (ctypes.c_size_t, [_P]),
         "fx_max_selected": (_I32, [_P]),
         "fx_unit_block_offset": (ctypes.c_int64, [_P, _I32]),
+        "fx_unit_summary_offset": (ctypes.c_int64, [_P, _I32]),
         "fx_split_tokens": (_I32, [_P]),
         "fx_status_string": (ctypes.c_char_p, [_I32]),
         "fx_read_error": (_I32, [_P, ctypes.POINTER(ctypes.c_uint32)]),
@@ -150,6 +153,7 @@ class Plan:
     workspace_bytes: int
     max_selected: int
     split_tokens: int
+    pooling: int = 0
 
     @property
     def units(self) -> int:
@@ -176,10 +180,13 @@ class Plan:
 
 
 def fx_plan_create(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: int, t_cap: int,
-                   dtype: int, policies: Sequence, split_tokens: int = 0) -> Plan:
-    """policies: one object per unit (u = b*Hkv + h) with the fields of fx_head_policy."""
+                   dtype: int, policies: Sequence, split_tokens: int = 0,
+                   pooling: int = 0) -> Plan:
+    """policies: one object per unit (u = b*Hkv + h) with the fields of fx_head_policy;
+    pooling: FX_POOL_KEY, FX_POOL_SCORE_SUM or FX_POOL_SCORE_MAX."""
     lib = load_library()
-    desc = _PlanDesc(batch, num_q_heads, num_kv_heads, head_dim, t_cap, dtype, split_tokens)
+    desc = _PlanDesc(batch, num_q_heads, num_kv_heads, head_dim, t_cap, dtype, split_tokens,
+                     pooling)
     arr = (_HeadPolicy * len(policies))()
     for i, p in enumerate(policies):
         arr[i] = _HeadPolicy(int(p.mode), int(p.block), int(p.sub_block), int(p.top_k),
@@ -194,13 +201,18 @@ def fx_plan_create(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: in
                 summary_bytes=lib.fx_summary_bytes(h), logits_bytes=lib.fx_logits_bytes(h),
                 evict_mask_bytes=lib.fx_evict_mask_bytes(h),
                 workspace_bytes=lib.fx_workspace_bytes(h), max_selected=lib.fx_max_selected(h),
-                split_tokens=lib.fx_split_tokens(h))
+                split_tokens=lib.fx_split_tokens(h), pooling=pooling)
 
 
 def fx_plan_destroy(plan: Plan) -> None:
     if plan.handle:
         _check("fx_plan_destroy", load_library().fx_plan_destroy(plan.handle))
         plan.handle = None
+
+
+def fx_unit_summary_offset(plan: Plan, unit: int) -> int:
+    """First summary row of a unit (-1 if out of range)."""
+    return int(load_library().fx_unit_summary_offset(plan.handle, int(unit)))
 
 
 def fx_read_error(plan: Plan) -> int:

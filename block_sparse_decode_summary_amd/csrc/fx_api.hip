@@ -42,6 +42,9 @@ fx_status check_desc(const fx_plan_desc* d) {
        d->split_tokens > fx::kMaxSplit))
     return FX_E_INVALID;
   if ((int64_t)d->batch * d->num_kv_heads > (1 << 20)) return FX_E_INVALID;
+  if (d->pooling != FX_POOL_KEY && d->pooling != FX_POOL_SCORE_SUM &&
+      d->pooling != FX_POOL_SCORE_MAX)
+    return FX_E_INVALID;
   // One unit's K (or V) rows are addressed with 32-bit byte offsets below 2^31.
   const int64_t unit_bytes = (int64_t)d->t_cap * d->head_dim * (d->dtype == FX_BF16 ? 2 : 4);
   if (unit_bytes > 0x7FFFFFFF) return FX_E_UNSUPPORTED;
@@ -98,6 +101,9 @@ fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_pl
     st = check_policy(pol[u]);
     if (st != FX_OK) return st;
   }
+  if (desc->pooling != FX_POOL_KEY)
+    for (int u = 0; u < units; ++u)
+      if (pol[u].block / pol[u].sub_block > fx::kMaxScoreRows) return FX_E_UNSUPPORTED;
 
   fx_plan* p = new (std::nothrow) fx_plan();
   if (!p) return FX_E_HIP;
@@ -105,7 +111,7 @@ fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_pl
   p->G = desc->num_q_heads / desc->num_kv_heads;
   p->units = units;
   p->host_units.resize(units);
-  int64_t boff = 0, moff = 0, max_sel = 1, max_ncap = 0, max_nfull = 0, work = 0;
+  int64_t boff = 0, soff = 0, moff = 0, max_sel = 1, max_ncap = 0, max_nfull = 0, work = 0;
   for (int u = 0; u < units; ++u) {
     const fx_head_policy& q = pol[u];
     UnitInfo& ui = p->host_units[u];
@@ -126,7 +132,11 @@ fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_pl
     ui.n_cap = (int32_t)n_cap;
     ui.mask_off = (int32_t)moff;
     ui.block_off = boff;
+    ui.log2r = desc->pooling == FX_POOL_KEY ? 0 : log2i(q.block / q.sub_block);
+    ui.reserved = 0;
+    ui.sum_off = soff;
     boff += n_cap;
+    soff += n_cap << ui.log2r;
     moff += ceil_div(n_cap, 32);
     max_sel = std::max(max_sel, ms);
     max_ncap = std::max(max_ncap, n_cap);
@@ -138,6 +148,8 @@ fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_pl
       p->host_scored.push_back(u);
       p->max_scored_n_full_cap =
           std::max<int32_t>(p->max_scored_n_full_cap, (int32_t)(desc->t_cap / q.block));
+      p->max_scored_rows_cap = std::max<int32_t>(
+          p->max_scored_rows_cap, (int32_t)((desc->t_cap / q.block) << ui.log2r));
     }
     if (q.mode == FX_NOSA && q.k_evict > 0) p->needs_logits = true;
     if (q.mode == FX_NOSA) p->any_nosa = true;
@@ -147,6 +159,7 @@ fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_pl
     return FX_E_UNSUPPORTED;
   }
   p->total_blocks = boff;
+  p->summary_rows = soff;
   p->mask_words = moff;
   p->max_sel = (int32_t)max_sel;
   p->max_n_cap = (int32_t)max_ncap;
@@ -235,7 +248,7 @@ fx_status fx_plan_destroy(fx_plan_t plan) {
 
 size_t fx_summary_bytes(fx_plan_t p) {
   if (!p) return 0;
-  return (size_t)p->total_blocks * p->desc.head_dim * (p->desc.dtype == FX_BF16 ? 2 : 4);
+  return (size_t)p->summary_rows * p->desc.head_dim * (p->desc.dtype == FX_BF16 ? 2 : 4);
 }
 size_t fx_logits_bytes(fx_plan_t p) { return p ? (size_t)p->total_blocks * 4 : 0; }
 size_t fx_evict_mask_bytes(fx_plan_t p) { return p ? (size_t)p->mask_words * 4 : 0; }
@@ -245,6 +258,10 @@ int32_t fx_split_tokens(fx_plan_t p) { return p ? p->split : -1; }
 int64_t fx_unit_block_offset(fx_plan_t p, int32_t unit) {
   if (!p || unit < 0 || unit >= p->units) return -1;
   return p->host_units[unit].block_off;
+}
+int64_t fx_unit_summary_offset(fx_plan_t p, int32_t unit) {
+  if (!p || unit < 0 || unit >= p->units) return -1;
+  return p->host_units[unit].sum_off;
 }
 
 const char* fx_status_string(fx_status s) {

@@ -39,8 +39,13 @@ struct UnitInfo {
   int32_t n_cap;       // ceil(t_cap / g)
   int32_t mask_off;    // first eviction-mask word of the unit
   int64_t block_off;   // first block slot of the unit in the packed per-block arrays
+  int32_t log2r;       // log2 of the summary rows per block (0 under key-side pooling)
+  int32_t reserved;
+  int64_t sum_off;     // first summary row of the unit
 };
-static_assert(sizeof(UnitInfo) == 64, "UnitInfo is read as one 64-byte record");
+static_assert(sizeof(UnitInfo) == 80, "UnitInfo layout");
+
+constexpr int kMaxScoreRows = 64;     // summary rows per block under score-side pooling
 
 }  // namespace fx
 
@@ -58,8 +63,10 @@ struct fx_plan {
   int32_t* d_scored = nullptr;   // retrieval and NOSA units, ascending
   int32_t n_scored = 0;
   int32_t max_scored_n_full_cap = 0;   // max over scored units of t_cap / g
+  int32_t max_scored_rows_cap = 0;     // max over scored units of (t_cap / g) * r
 
   int64_t total_blocks = 0;
+  int64_t summary_rows = 0;      // sum over units of n_cap * r
   int64_t mask_words = 0;
   int32_t max_sel = 0;
   int32_t max_n_cap = 0;

@@ -14,14 +14,23 @@
 // off below).  This is the group's sum of raw dot products with the summary; the fixed
 // order makes the float32 value, and hence the selection, reproducible bit for bit.
 //
+// Score-side pooling (the block max taken over scores): the block has r summary rows
+// M_u (its sub-block means), and
+//   group sum: score = (float) max over u of acc(qs, M_u)
+//   group max: score = (float) max over u and g of acc(q_g, M_u)
+// acc being the chain above with the given vector.  Rounding is monotone, so each row's
+// value is rounded first and the max is taken over floats.  A lane scores one row; the
+// r rows of a block are r adjacent lanes (r divides 64), whose max is a butterfly.
+//
 // Mapping: the grid covers only retrieval and NOSA units (a host-built list); one
-// 256-thread workgroup takes four consecutive 64-block tiles of a unit, one tile per
-// wave and one block per lane, and forms the float64 group sum qs once for all four.
+// 256-thread workgroup takes four consecutive 64-row tiles of a unit's summary rows,
+// one tile per wave and one row per lane, and forms the float64 group sum qs (or the
+// G float64 query rows, for the group max) once for all four.
 // The unit index varies fastest along the grid: workgroup i runs on XCD i mod 8, so
 // this spreads the first tile groups (present for every unit) over all eight XCDs
 // instead of stacking them on one.
 // Each wave requests its whole tile at once through a buffer resource bounded to the
-// unit's full blocks (rows past the end read as zero without a memory access), in
+// rows of the unit's full blocks (rows past the end read as zero without a memory access), in
 // column-chunk order: chunk ch holds columns [ch*C, ch*C + C) of all 64 rows, C being
 // 32 words, and one load instruction covers eight 128-byte row segments.  The chunks
 // then pass one at a time through a per-wave LDS tile with stride 33 words (33 is odd,
@@ -41,11 +50,17 @@ __device__ __forceinline__ double elem_f64(const uint32_t* row, int c, bf16_t*) 
   return (double)((c & 1) ? bf16_hi(w) : bf16_lo(w));
 }
 
-constexpr int kTile = 64;         // blocks per tile (one per lane)
+constexpr int kTile = 64;         // summary rows per tile (one per lane)
 constexpr int kWaves = 4;         // tiles per workgroup (one per wave)
 constexpr int kChunkWords = 32;   // row words staged in LDS at a time
 
-template <typename E, int D>
+// NaN-propagating max (a NaN score is flagged later by the selection).
+__device__ __forceinline__ double max_nan(double a, double b) { return (a != a || a >= b) ? a : b; }
+__device__ __forceinline__ float max_nan(float a, float b) { return (a != a || a >= b) ? a : b; }
+
+// GM = 0: the group's rows are summed (G is a runtime value); GM = 1..8: the group of
+// GM rows is aggregated by a max.
+template <typename E, int D, int GM>
 __global__ __launch_bounds__(kWaves * 64) void k_score(
     const UnitInfo* __restrict__ units, const int32_t* __restrict__ scored,
     const E* __restrict__ q, const E* __restrict__ S, const int32_t* __restrict__ seq_lens,
@@ -67,19 +82,22 @@ __global__ __launch_bounds__(kWaves * 64) void k_score(
   const int b = u / Hkv, h = u % Hkv;
   const int T = load_seq_len(seq_lens, b, t_cap, err);
   const int n_full = T >> ui.log2g;
+  const int log2r = ui.log2r;
+  const int n_rows = n_full << log2r;
   const int tile0 = quad * kWaves;
-  if (tile0 * kTile >= n_full) return;
+  if (tile0 * kTile >= n_rows) return;
   const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int j0 = (tile0 + w) * kTile;
 
   __shared__ uint32_t rows[kWaves][kTile][kChunkWords + 1];
   __shared__ uint4 qrows[kMaxGroup * QV4];
-  __shared__ double qs[D];
+  constexpr int NV = GM == 0 ? 1 : GM;          // query vectors of the chains
+  __shared__ double qs[NV * D];
 
   // The whole tile, chunk by chunk: piece m = lane + 64k of chunk ch is row m / CPIECES,
   // 16-byte piece ch*CPIECES + m % CPIECES.
   const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(S + (size_t)ui.block_off * D), 0, n_full * ROW_BYTES, kRsrcWord3);
+      (void*)(S + (size_t)ui.sum_off * D), 0, n_rows * ROW_BYTES, kRsrcWord3);
   uint4 buf[NCH][PER_LANE];
 #pragma unroll
   for (int ch = 0; ch < NCH; ++ch)
@@ -99,12 +117,19 @@ __global__ __launch_bounds__(kWaves * 64) void k_score(
   const E* qe = reinterpret_cast<const E*>(qrows);
   if ((int)threadIdx.x < D) {
     const int c = threadIdx.x;
-    double a = (double)to_f32(qe[c]);
-    for (int g = 1; g < G; ++g) a = a + (double)to_f32(qe[g * D + c]);
-    qs[c] = a;
+    if constexpr (GM == 0) {
+      double a = (double)to_f32(qe[c]);
+      for (int g = 1; g < G; ++g) a = a + (double)to_f32(qe[g * D + c]);
+      qs[c] = a;
+    } else {
+#pragma unroll
+      for (int g = 0; g < GM; ++g) qs[g * D + c] = (double)to_f32(qe[g * D + c]);
+    }
   }
 
-  double acc = 0.0;
+  double acc[NV];
+#pragma unroll
+  for (int g = 0; g < NV; ++g) acc[g] = 0.0;
 #pragma unroll
   for (int ch = 0; ch < NCH; ++ch) {
 #pragma unroll
@@ -122,26 +147,54 @@ __global__ __launch_bounds__(kWaves * 64) void k_score(
 #pragma clang fp contract(off)
 #pragma unroll 16
       for (int c = 0; c < CCOLS; ++c) {
-        const double prod = qs[ch * CCOLS + c] * elem_f64(row, c, (E*)nullptr);
-        acc = acc + prod;
+        const double x = elem_f64(row, c, (E*)nullptr);
+#pragma unroll
+        for (int g = 0; g < NV; ++g) {
+          const double prod = qs[g * D + ch * CCOLS + c] * x;
+          acc[g] = acc[g] + prod;
+        }
       }
     }
     __syncthreads();
   }
-  if (j0 + lane < n_full) scores[(size_t)ui.block_off + j0 + lane] = (float)acc;
+  double v = acc[0];
+#pragma unroll
+  for (int g = 1; g < NV; ++g) v = max_nan(v, acc[g]);
+  float f = (float)v;
+  for (int off = 1; off < (1 << log2r); off <<= 1) f = max_nan(f, __shfl_xor(f, off));
+  const int row = j0 + lane;
+  if ((lane & ((1 << log2r) - 1)) == 0 && row < n_rows)
+    scores[(size_t)ui.block_off + (row >> log2r)] = f;
+}
+
+template <typename E, int D, int GM>
+hipError_t launch_gm(const fx_plan* p, const void* q, const void* S, const int32_t* seq_lens,
+                     float* scores, hipStream_t stream) {
+  const int tiles = (p->max_scored_rows_cap + kTile - 1) / kTile;
+  const int quads = (tiles + kWaves - 1) / kWaves;
+  if (quads == 0 || p->n_scored == 0) return hipSuccess;
+  const dim3 grid((unsigned)((int64_t)quads * p->n_scored));
+  k_score<E, D, GM><<<grid, kWaves * 64, 0, stream>>>(
+      p->d_units, p->d_scored, static_cast<const E*>(q), static_cast<const E*>(S), seq_lens,
+      scores, p->d_error, p->desc.num_kv_heads, p->G, p->desc.t_cap, quads);
+  return hipGetLastError();
 }
 
 template <typename E, int D>
 hipError_t launch_t(const fx_plan* p, const void* q, const void* S, const int32_t* seq_lens,
                     float* scores, hipStream_t stream) {
-  const int tiles = (p->max_scored_n_full_cap + kTile - 1) / kTile;
-  const int quads = (tiles + kWaves - 1) / kWaves;
-  if (quads == 0 || p->n_scored == 0) return hipSuccess;
-  const dim3 grid((unsigned)((int64_t)quads * p->n_scored));
-  k_score<E, D><<<grid, kWaves * 64, 0, stream>>>(
-      p->d_units, p->d_scored, static_cast<const E*>(q), static_cast<const E*>(S), seq_lens,
-      scores, p->d_error, p->desc.num_kv_heads, p->G, p->desc.t_cap, quads);
-  return hipGetLastError();
+  if (p->desc.pooling != FX_POOL_SCORE_MAX)
+    return launch_gm<E, D, 0>(p, q, S, seq_lens, scores, stream);
+  switch (p->G) {
+    case 1: return launch_gm<E, D, 1>(p, q, S, seq_lens, scores, stream);
+    case 2: return launch_gm<E, D, 2>(p, q, S, seq_lens, scores, stream);
+    case 3: return launch_gm<E, D, 3>(p, q, S, seq_lens, scores, stream);
+    case 4: return launch_gm<E, D, 4>(p, q, S, seq_lens, scores, stream);
+    case 5: return launch_gm<E, D, 5>(p, q, S, seq_lens, scores, stream);
+    case 6: return launch_gm<E, D, 6>(p, q, S, seq_lens, scores, stream);
+    case 7: return launch_gm<E, D, 7>(p, q, S, seq_lens, scores, stream);
+    default: return launch_gm<E, D, 8>(p, q, S, seq_lens, scores, stream);
+  }
 }
 
 }  // namespace

@@ -12,10 +12,15 @@
 // division by the power-of-two s is exact; the max is exact; the one rounding into the
 // storage type is to nearest, ties to even (f64_to_bf16_rne / cvt_f32_f64).
 //
+// Score-side pooling (the block-level max taken later, over scores) keeps the means:
+//   S[j*r + u][c] = round_once( ( sum of the s rows of u )[c] / s ),  r = g / s,
+// written at the unit's summary rows instead of the max.
+//
 // Mapping: one 256-thread workgroup per (unit, block).  A key row is WORDS 32-bit
 // words (d * sizeof(elem) / 4); thread (w, ph) owns word w and the sub-blocks
 // u = ph, ph + PH, ...  Each wave reads whole rows (coalesced 4-byte lanes); the
-// sub-block maxima of the PH phases meet in LDS.
+// sub-block maxima of the PH phases meet in LDS (key side), or every thread stores
+// its own means (score side).
 #include "fx_device.h"
 
 namespace fx {
@@ -39,7 +44,7 @@ template <typename E, int D>
 __global__ __launch_bounds__(256) void k_build_summaries(
     const UnitInfo* __restrict__ units, const E* __restrict__ K,
     const int32_t* __restrict__ seq_lens, int32_t bb, int32_t be, E* __restrict__ S,
-    uint32_t* __restrict__ err, int Hkv, int t_cap, int blocks_per_unit) {
+    uint32_t* __restrict__ err, int Hkv, int t_cap, int blocks_per_unit, bool score_side) {
   constexpr int WORDS = D * (int)sizeof(E) / 4;
   constexpr int EPW = 4 / (int)sizeof(E);
   constexpr int PH = 256 / WORDS;
@@ -76,9 +81,16 @@ __global__ __launch_bounds__(256) void k_build_summaries(
 #pragma unroll
       for (int e = 0; e < EPW; ++e) acc[e] += v[e];
     }
+    if (score_side) {
+      E* dst = S + ((size_t)ui.sum_off + ((size_t)j << ui.log2r) + sb) * D + (size_t)w * EPW;
+#pragma unroll
+      for (int e = 0; e < EPW; ++e) store_from_f64(dst + e, acc[e] * inv_s);
+      continue;
+    }
 #pragma unroll
     for (int e = 0; e < EPW; ++e) mx[e] = fmax(mx[e], acc[e] * inv_s);
   }
+  if (score_side) return;   // uniform across the workgroup
 
   __shared__ double red[PH][WORDS * EPW];
 #pragma unroll
@@ -91,7 +103,7 @@ __global__ __launch_bounds__(256) void k_build_summaries(
     for (int i = 1; i < PH; ++i) m = fmax(m, red[i][w * EPW + e]);
     mx[e] = m;
   }
-  E* dst = S + ((size_t)ui.block_off + (size_t)j) * D + (size_t)w * EPW;
+  E* dst = S + ((size_t)ui.sum_off + (size_t)j) * D + (size_t)w * EPW;
 #pragma unroll
   for (int e = 0; e < EPW; ++e) store_from_f64(dst + e, mx[e]);
 }
@@ -102,7 +114,7 @@ hipError_t launch_t(const fx_plan* p, const void* K, const int32_t* seq_lens, in
   const dim3 grid((unsigned)((int64_t)blocks_per_unit * p->units));
   k_build_summaries<E, D><<<grid, 256, 0, stream>>>(
       p->d_units, static_cast<const E*>(K), seq_lens, bb, be, static_cast<E*>(S), p->d_error,
-      p->desc.num_kv_heads, p->desc.t_cap, blocks_per_unit);
+      p->desc.num_kv_heads, p->desc.t_cap, blocks_per_unit, p->desc.pooling != FX_POOL_KEY);
   return hipGetLastError();
 }
 

@@ -44,8 +44,12 @@
  *
  *   Per-block arrays are packed per unit: unit u owns n_cap(u) consecutive slots
  *   starting at block_off(u) = sum over u' < u of n_cap(u').  In this layout:
- *     summaries     elem [total_blocks][d]       (slot = block_off(u) + j)
  *     evict_logits  float32 [total_blocks]
+ *   Summaries have r(u) rows per block slot: r = 1 under FX_POOL_KEY, block /
+ *   sub_block under score-side pooling.  Unit u owns n_cap(u) * r(u) rows starting at
+ *   row sum_off(u) = sum over u' < u of n_cap(u') * r(u'); block j's rows are
+ *   sum_off(u) + j*r .. + r - 1 (sum_off = block_off under FX_POOL_KEY):
+ *     summaries     elem [summary_rows][d]
  *   The eviction mask packs ceil(n_cap(u)/32) uint32 words per unit starting at
  *   word mask_off(u) = sum over u' < u of ceil(n_cap(u')/32); block j of unit u is
  *   bit (j % 32) of word mask_off(u) + j / 32.  Bits set = evicted.
@@ -106,6 +110,18 @@ enum { FX_F32 = 0, FX_BF16 = 1 };
  *                 logit (Γe) with strict eviction ([NOSA-DE] Methodik §1).          */
 enum { FX_RETRIEVAL = 0, FX_STREAMING = 1, FX_NOSA = 2 };
 
+/* Where the block-level max of the two-stage pooling acts ([NOSA-DE] Methodik §1,
+ * "Blockweise Implementierung": mean inside sub-blocks, then max at block level).
+ *   FX_POOL_KEY:       on the key side.  One summary row per block, the elementwise max
+ *                      of its sub-block means; the score sums the group's dot products
+ *                      with it.
+ *   FX_POOL_SCORE_SUM: on the score side.  r = block / sub_block summary rows per block,
+ *                      one per sub-block mean; the score is the max over them of the
+ *                      group's summed dot product.
+ *   FX_POOL_SCORE_MAX: as FX_POOL_SCORE_SUM with the group aggregated by a max over its
+ *                      G query rows instead of a sum.                                   */
+enum { FX_POOL_KEY = 0, FX_POOL_SCORE_SUM = 1, FX_POOL_SCORE_MAX = 2 };
+
 /* Error-word bits (fx_read_error). */
 enum {
   FX_ERR_SEQ_LEN = 1u << 0,        /* a seq_len was outside [0, t_cap]; clamped */
@@ -125,6 +141,9 @@ typedef struct {
   int32_t dtype;           /* FX_F32 or FX_BF16: element type of q, K, V, summaries, out */
   int32_t split_tokens;    /* fewest selected tokens per decode workgroup (a power of two,
                               64..2048), 0 = automatic (256) */
+  int32_t pooling;         /* FX_POOL_KEY (0), FX_POOL_SCORE_SUM or FX_POOL_SCORE_MAX; the
+                              score-side kinds need block / sub_block <= 64 in every unit
+                              (else FX_E_UNSUPPORTED) */
 } fx_plan_desc;
 
 /* Per-unit selection policy.  Blocks of one unit are `block` tokens (a power of
@@ -169,12 +188,13 @@ fx_status fx_plan_create(const fx_plan_desc* desc, const fx_head_policy* host_po
 fx_status fx_plan_destroy(fx_plan_t plan);
 
 /* Sizes derived from the plan (0 / -1 for a NULL plan). */
-size_t fx_summary_bytes(fx_plan_t plan);       /* total_blocks * d * sizeof(elem) */
+size_t fx_summary_bytes(fx_plan_t plan);       /* summary_rows * d * sizeof(elem) */
 size_t fx_logits_bytes(fx_plan_t plan);        /* total_blocks * 4 */
 size_t fx_evict_mask_bytes(fx_plan_t plan);    /* total mask words * 4 */
 size_t fx_workspace_bytes(fx_plan_t plan);     /* workspace for fx_select and fx_sparse_decode */
 int32_t fx_max_selected(fx_plan_t plan);       /* max_sel: row stride of sel_idx and delta lists */
 int64_t fx_unit_block_offset(fx_plan_t plan, int32_t unit);   /* block_off(u), -1 if out of range */
+int64_t fx_unit_summary_offset(fx_plan_t plan, int32_t unit); /* sum_off(u), -1 if out of range */
 int32_t fx_split_tokens(fx_plan_t plan);       /* the split_tokens value the plan uses */
 
 const char* fx_status_string(fx_status status);
@@ -202,7 +222,10 @@ fx_status fx_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStrea
  * resolved per unit like a Python slice against n_full (negative values count
  * from n_full; both ends are clamped to [0, n_full]); (0, INT32_MAX) is every full
  * block, (-1, INT32_MAX) the newest one.  Slots outside the range are untouched.
- * K: elem [B][Hkv][t_cap][d]; summaries: elem [total_blocks][d] (fx_summary_bytes). */
+ * Under score-side pooling (FX_POOL_SCORE_*) the max is not taken here: block j's r
+ * summary rows are the r sub-block means, each rounded once:
+ *     S[j*r + u][c] = round_once( (sum of the s rows of sub-block u)[c] / s ).
+ * K: elem [B][Hkv][t_cap][d]; summaries: elem [summary_rows][d] (fx_summary_bytes). */
 fx_status fx_build_summaries(fx_plan_t plan, const void* K, const int32_t* seq_lens,
                              int32_t block_begin, int32_t block_end, void* summaries,
                              hipStream_t stream);
@@ -217,7 +240,12 @@ fx_status fx_build_summaries(fx_plan_t plan, const void* K, const int32_t* seq_l
  *                                               every product and sum rounded (no FMA)
  *     score = (float)acc                        round to nearest, ties to even
  * i.e. the sum over the group of the raw dot products with the summary (no
- * 1/sqrt(d), no softmax).  Then per unit, with F the forced set (see fx_head_policy):
+ * 1/sqrt(d), no softmax).  Under score-side pooling the same chain runs over each of
+ * the block's r summary rows M_u and
+ *     FX_POOL_SCORE_SUM: score = (float) max over u of acc(qs, M_u)
+ *     FX_POOL_SCORE_MAX: score = (float) max over u and g of acc(q_g, M_u)
+ * (acc(v, M) being the chain above with v in place of qs).
+ * Then per unit, with F the forced set (see fx_head_policy):
  *   streaming : selection = F;
  *   retrieval : selection = F + the k best full blocks outside F by score;
  *   NOSA      : E = full blocks outside F not evicted; Γe = the k_evict best of E by

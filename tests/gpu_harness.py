@@ -31,7 +31,7 @@ def say(msg: str) -> None:
 def make_plan(w: Workload, split_tokens: int = 0) -> fx.Plan:
     dt = fx.FX_F32 if w.dtype == "f32" else fx.FX_BF16
     return fx.fx_plan_create(w.batch, w.num_q_heads, w.num_kv_heads, w.head_dim, w.t_cap, dt,
-                             list(w.policies), split_tokens)
+                             list(w.policies), split_tokens, w.pooling)
 
 
 def softmax_scale(w: Workload) -> float:
@@ -51,7 +51,7 @@ def run_select_decode(plan: fx.Plan, bufs: fx.StepBuffers, inp, q: torch.Tensor,
 
 @dataclass
 class GpuUnit:
-    summaries: np.ndarray     # float64 [n_full][d]
+    summaries: np.ndarray     # float64 [n_full][d] ([n_full][r][d] under score-side pooling)
     scores: Optional[np.ndarray]
     sel: np.ndarray
     out: np.ndarray           # float64 [G][d]
@@ -74,6 +74,7 @@ class GpuView:
         self.lse = bufs.lse.to("cpu").to(torch.float64).numpy().copy()
         self.mask = bufs.evicted_mask.to("cpu").numpy().view(np.uint32).copy()
         self.block_off = w.block_offsets()
+        self.sum_off = w.summary_row_offsets()
         self.mask_off = w.mask_word_offsets()
 
     def unit(self, u: int) -> GpuUnit:
@@ -84,9 +85,11 @@ class GpuView:
         g = w.policies[u].block
         n_full = T // g
         o = int(self.block_off[u])
+        so, r = int(self.sum_off[u]), w.summary_rows_per_block(u)
+        summ = self.summ[so:so + n_full * r]
         cnt = int(self.sel_cnt[u])
         return GpuUnit(
-            summaries=self.summ[o:o + n_full],
+            summaries=summ if w.pooling == 0 else summ.reshape(n_full, r, w.head_dim),
             scores=self.scores[o:o + n_full] if w.policies[u].mode != fx.FX_STREAMING else None,
             sel=self.sel_idx[u, :cnt].astype(np.int64),
             out=self.out[b, h * G:(h + 1) * G],
@@ -110,7 +113,7 @@ def oracle_unit(inp, u: int, q: torch.Tensor, evicted: Optional[np.ndarray] = No
     b, h = divmod(u, w.num_kv_heads)
     q_rows, K, V = unit_arrays(inp, b, h, q=q)
     return unit_step(w.policies[u], w.seq_lens[b], w.dtype, q_rows, K, V, softmax_scale(w),
-                     logits=unit_logits(inp, u), evicted=evicted, ed=ed)
+                     logits=unit_logits(inp, u), evicted=evicted, ed=ed, pooling=w.pooling)
 
 
 def assert_close(name: str, got: np.ndarray, ref: np.ndarray, rtol: float, atol: float) -> float:

@@ -54,12 +54,12 @@ class P:
 
 def _create(desc_kw=None, pol_kw=None, units=None):
     d = dict(batch=1, num_q_heads=4, num_kv_heads=2, head_dim=128, t_cap=1024, dtype=fx.FX_BF16,
-             split_tokens=0)
+             split_tokens=0, pooling=fx.FX_POOL_KEY)
     d.update(desc_kw or {})
     n = d["batch"] * d["num_kv_heads"] if units is None else units
     pols = [P(**(pol_kw or {})) for _ in range(n)]
     return fx.fx_plan_create(d["batch"], d["num_q_heads"], d["num_kv_heads"], d["head_dim"],
-                             d["t_cap"], d["dtype"], pols, d["split_tokens"])
+                             d["t_cap"], d["dtype"], pols, d["split_tokens"], d["pooling"])
 
 
 @pytest.mark.parametrize("desc_kw", [
@@ -67,6 +67,7 @@ def _create(desc_kw=None, pol_kw=None, units=None):
     dict(num_q_heads=18, num_kv_heads=2),                                      # G = 9
     dict(head_dim=96), dict(t_cap=0), dict(t_cap=(1 << 24) + 1), dict(dtype=7),
     dict(split_tokens=100), dict(split_tokens=32), dict(split_tokens=4096),
+    dict(pooling=3), dict(pooling=-1),
 ])
 def test_invalid_descriptions(lib, desc_kw):
     with pytest.raises(fx.FxError) as e:
@@ -86,6 +87,14 @@ def test_invalid_policies(lib, pol_kw):
     assert e.value.status == 1
 
 
+@pytest.mark.parametrize("pooling", [fx.FX_POOL_SCORE_SUM, fx.FX_POOL_SCORE_MAX])
+def test_score_side_pooling_limits_rows_per_block(lib, pooling):
+    """Score-side pooling keeps block / sub_block summary rows per block, at most 64."""
+    with pytest.raises(fx.FxError) as e:
+        _create(desc_kw=dict(pooling=pooling), pol_kw=dict(block=256, sub_block=2))
+    assert e.value.status == 2
+
+
 def test_null_arguments_rejected_on_host(lib):
     # NULL plan / NULL output pointer: FX_E_INVALID without touching a device.
     assert lib.fx_plan_create(None, None, None) == 1
@@ -97,3 +106,6 @@ def test_null_arguments_rejected_on_host(lib):
     assert lib.fx_workspace_bytes(None) == 0 and lib.fx_max_selected(None) == -1
     assert lib.fx_plan_destroy(None) == 0
     assert lib.fx_unit_block_offset(None, 0) == -1
+    assert lib.fx_unit_summary_offset(None, 0) == -1
+    assert lib.fx_sparse_decode_ed(None, *([None] * 7), ctypes.c_float(1.0), None, None, None, 0,
+                                   None) == 1

@@ -64,6 +64,7 @@ class Workload:
     steps: int = 1
     drift: Optional[Tuple[float, float]] = None   # (decay, noise) of the query drift
     description: str = ""
+    pooling: int = 0                    # 0 key-side; 1 / 2 score-side with group sum / max
 
     @property
     def group(self) -> int:
@@ -85,6 +86,17 @@ class Workload:
         caps = np.array([self.n_cap(u) for u in range(self.num_units)], dtype=np.int64)
         off = np.zeros(self.num_units + 1, dtype=np.int64)
         off[1:] = np.cumsum(caps)
+        return off
+
+    def summary_rows_per_block(self, u: int) -> int:
+        p = self.policies[u]
+        return 1 if self.pooling == 0 else p.block // p.sub_block
+
+    def summary_row_offsets(self) -> np.ndarray:
+        rows = np.array([self.n_cap(u) * self.summary_rows_per_block(u)
+                         for u in range(self.num_units)], dtype=np.int64)
+        off = np.zeros(self.num_units + 1, dtype=np.int64)
+        off[1:] = np.cumsum(rows)
         return off
 
     def mask_word_offsets(self) -> np.ndarray:
