@@ -30,5 +30,7 @@ Modules
   selection  forced sets, top-k per kv head, NOSA eviction selection
   attention  attention over the selected tokens; split-K partial merge
   delta      selection set differences and locality
+  compaction the selected full blocks kept in a block-slot working set (moves by set
+             difference)
   step       one decode step for one unit / a whole workload
 """

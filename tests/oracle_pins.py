@@ -576,6 +576,73 @@ def check_biased_attention(attend, token_bias, selected_tokens, merge_partials, 
 
 
 # ----------------------------------------------------------------------------------------
+# compaction
+# ----------------------------------------------------------------------------------------
+
+def check_compaction(compact_update, apply_moves, selection_delta):
+    """Block-slot working set of the selected full blocks, moved by set difference."""
+    # Hand example, g = 4, five slots.
+    m, mv = compact_update(np.full(5, -1), np.array([0, 2, 5, 7]), 30, 4)   # block 7 partial
+    assert list(m) == [0, 2, 5, -1, -1] and mv == [(0, 0), (1, 2), (2, 5)]
+    m, mv = compact_update(m, np.array([0, 3, 5, 7]), 31, 4)                # 2 out, 3 in
+    assert list(m) == [0, 3, 5, -1, -1] and mv == [(1, 3)]
+    m, mv = compact_update(m, np.array([0, 5, 7]), 32, 4)                   # 7 became full
+    assert list(m) == [0, 7, 5, -1, -1] and mv == [(1, 7)]
+    m2, mv = compact_update(m, np.array([0, 5, 7]), 33, 4)                  # nothing new
+    assert list(m2) == list(m) and mv == []
+    m3, mv = compact_update(m, np.zeros(0, np.int64), 33, 4)
+    assert list(m3) == [-1] * 5 and mv == []
+    try:
+        compact_update(np.full(2, -1), np.array([0, 1, 2]), 40, 4)
+        raise AssertionError("capacity not enforced")
+    except ValueError:
+        pass
+
+    # Random growing sequences against independent characterisations.
+    rng = np.random.default_rng(26)
+    for trial in range(60):
+        g = int(rng.choice([1, 4, 16]))
+        n_slots = int(rng.integers(3, 12))
+        T = int(rng.integers(0, 6 * g))
+        d = 3
+        K = rng.standard_normal((T + 80 * g, d))
+        V = rng.standard_normal((T + 80 * g, d))
+        slots = np.full(n_slots, -1)
+        wK = np.full((n_slots * g, d), np.nan)
+        wV = np.full((n_slots * g, d), np.nan)
+        prev_full = np.zeros(0, np.int64)
+        for step in range(12):
+            T += int(rng.integers(0, 2 * g))
+            n_tot, n_full = -(-T // g), T // g
+            k = int(rng.integers(0, min(n_slots, n_full) + 1))
+            sel = np.sort(rng.choice(n_full, size=k, replace=False)) if k else np.zeros(0, np.int64)
+            if n_tot > n_full and rng.random() < 0.7:
+                sel = np.append(sel, n_tot - 1)                   # the partial last block
+            before = slots.copy()
+            slots, mv = compact_update(slots, sel, T, g)
+            target = sel[sel < n_full]
+            held_before = before[before >= 0]
+            assert sorted(slots[slots >= 0].tolist()) == sorted(target.tolist())
+            for s_, b in enumerate(before):                      # kept blocks stay put
+                if b >= 0 and b in target:
+                    assert slots[s_] == b
+            added = np.setdiff1d(target, held_before)
+            assert [b for _, b in mv] == list(added)             # ascending, only the new ones
+            free_after_removal = [s_ for s_ in range(n_slots)
+                                  if before[s_] < 0 or before[s_] not in target]
+            assert [s_ for s_, _ in mv] == free_after_removal[:len(added)]
+            apply_moves(wK, wV, K, V, mv, g)
+            for s_, b in enumerate(slots):                       # contents: brute force
+                if b >= 0:
+                    assert np.array_equal(wK[s_ * g:(s_ + 1) * g], K[b * g:(b + 1) * g])
+                    assert np.array_equal(wV[s_ * g:(s_ + 1) * g], V[b * g:(b + 1) * g])
+            # with only full blocks on both sides, the moves are the selection delta's adds.
+            assert list(added) == list(selection_delta(prev_full, target)[0]) or \
+                len(np.setdiff1d(held_before, prev_full)) > 0
+            prev_full = target
+
+
+# ----------------------------------------------------------------------------------------
 # delta
 # ----------------------------------------------------------------------------------------
 

@@ -8,7 +8,7 @@ import math
 import numpy as np
 import pytest
 
-from oracle import attention, delta, numerics, pooling, scoring, selection
+from oracle import attention, compaction, delta, numerics, pooling, scoring, selection
 
 import oracle_pins as pins
 
@@ -408,6 +408,69 @@ def test_biased_attention_mutants(which):
         tb = _token_bias_full_blocks
     assert _fails(pins.check_biased_attention, att, tb, attention.selected_tokens,
                   attention.merge_partials, part)
+
+
+# ---- compaction -----------------------------------------------------------------------
+
+def _compact_free_descending(slot_map, sel, T, g):
+    slots = np.array(slot_map, dtype=np.int64, copy=True)
+    target = compaction.held_target(sel, T, g)
+    for s in range(slots.size):
+        if slots[s] >= 0 and slots[s] not in target:
+            slots[s] = -1
+    added = [int(b) for b in target if b not in slots]
+    free = [s for s in range(slots.size) if slots[s] < 0][::-1]
+    moves = sorted(zip(free[:len(added)], added))
+    for s, b in moves:
+        slots[s] = b
+    return slots, moves
+
+
+def _compact_move_everything(slot_map, sel, T, g):          # re-copies held blocks too
+    target = compaction.held_target(sel, T, g)
+    slots = np.full(len(slot_map), -1)
+    moves = [(i, int(b)) for i, b in enumerate(target)]
+    for s, b in moves:
+        slots[s] = b
+    return slots, moves
+
+
+def _compact_holds_partial(slot_map, sel, T, g):            # the growing block is held too
+    return compaction.compact_update(slot_map, sel, T + g - 1 if T % g else T, g)
+
+
+def _compact_no_free(slot_map, sel, T, g):                  # deselected blocks keep slots
+    slots = np.array(slot_map, dtype=np.int64, copy=True)
+    target = compaction.held_target(sel, T, g)
+    added = [int(b) for b in target if b not in slots]
+    free = [s for s in range(slots.size) if slots[s] < 0]
+    if len(added) > len(free):
+        raise ValueError("full")
+    moves = list(zip(free[:len(added)], added))
+    for s, b in moves:
+        slots[s] = b
+    return slots, moves
+
+
+def _apply_moves_keys_only(wK, wV, K, V, moves, g):
+    for s, b in moves:
+        wK[s * g:(s + 1) * g] = K[b * g:(b + 1) * g]
+
+
+@pytest.mark.parametrize("which", ["free_desc", "move_all", "partial", "no_free", "keys_only"])
+def test_compaction_mutants(which):
+    cu, am = compaction.compact_update, compaction.apply_moves
+    if which == "free_desc":
+        cu = _compact_free_descending
+    elif which == "move_all":
+        cu = _compact_move_everything
+    elif which == "partial":
+        cu = _compact_holds_partial
+    elif which == "no_free":
+        cu = _compact_no_free
+    else:
+        am = _apply_moves_keys_only
+    assert _fails(pins.check_compaction, cu, am, delta.selection_delta)
 
 
 # ---- delta ----------------------------------------------------------------------------

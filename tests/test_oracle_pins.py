@@ -2,7 +2,7 @@
 import numpy as np
 import pytest
 
-from oracle import attention, delta, numerics, pooling, scoring, selection
+from oracle import attention, compaction, delta, numerics, pooling, scoring, selection
 from oracle.step import unit_step
 
 import oracle_pins as pins
@@ -116,6 +116,10 @@ def test_unit_step_score_side_pooling():
         assert r.summaries.shape == (T // 32, 4, d)
         assert np.array_equal(r.scores, scoring.sub_block_scores(
             q, pooling.sub_block_means(K, 32, 8, "bf16"), pool))
+
+
+def test_compaction():
+    pins.check_compaction(compaction.compact_update, compaction.apply_moves, delta.selection_delta)
 
 
 def test_delta():
