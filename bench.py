@@ -175,6 +175,9 @@ def main() -> int:
     ap.add_argument("--pooling", choices=["key", "score_sum", "score_max"], default="key",
                     help="where the block max of the two-stage pooling acts: over key vectors "
                          "(one summary row per block) or over the scores of the sub-block means")
+    ap.add_argument("--compact", action="store_true",
+                    help="after the delta, keep the selected full blocks in a block-slot working "
+                         "set (fx_compact_update), timed as its own phase")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-reference", action="store_true",
@@ -220,6 +223,7 @@ def main() -> int:
     mask = A.evicted_mask if w.has_nosa else None
     fx.fx_build_summaries(plan, inp.K, inp.seq_lens, 0, INT32_MAX, A.summaries)   # prefill
     flush_buf = None if args.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    wset = fx.allocate_working_set(plan, dev) if args.compact else None
 
     cur, prev = A, Bsel
     lens = list(w.seq_lens)
@@ -241,11 +245,19 @@ def main() -> int:
         ev_d1[i].record()
         fx.fx_selection_delta(plan, prev.sel_idx, prev.sel_cnt, cur.sel_idx, cur.sel_cnt,
                               A.added, A.added_cnt, A.removed, A.removed_cnt)
+        if wset is not None:
+            ev_c0[i].record()
+            fx.fx_compact_update(plan, inp.K, inp.V, inp.seq_lens, cur.sel_idx, cur.sel_cnt, wset,
+                                 A.workspace)
+            ev_c1[i].record()
+            hist_moved[i].copy_(wset.moved_cnt)
         cur, prev = prev, cur
 
     n_ev = args.warmup + args.steps
     mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
     ev_s0, ev_s1, ev_b1, ev_d0, ev_d1 = mk(), mk(), mk(), mk(), mk()
+    ev_c0, ev_c1 = (mk(), mk()) if args.compact else (None, None)
+    hist_moved = torch.zeros(n_ev, w.num_units, dtype=torch.int32, device=dev) if args.compact else None
     # Per-step selection statistics of multi-step (drifting query) workloads, copied out
     # after each step's end event.
     multi = len(qs) > 1
@@ -282,9 +294,11 @@ def main() -> int:
         "build": [ev_s0[i].elapsed_time(ev_b1[i]) for i in timed],
         "select": [ev_b1[i].elapsed_time(ev_d0[i]) for i in timed],
         "decode": dec_ms,
-        "delta": [ev_d1[i].elapsed_time(ev_s1[i]) for i in timed],
+        "delta": [ev_d1[i].elapsed_time(ev_c0[i] if args.compact else ev_s1[i]) for i in timed],
         "select_decode": [ev_b1[i].elapsed_time(ev_d1[i]) for i in timed],
     }
+    if args.compact:
+        phases["compact"] = [ev_c0[i].elapsed_time(ev_c1[i]) for i in timed]
     ms_per_step = float(np.mean(step_ms))
     dec_avg = float(np.mean(dec_ms))
     if fx.fx_read_error(plan) != 0:
@@ -331,8 +345,26 @@ def main() -> int:
     sel_idx = prev.sel_idx.cpu().numpy()      # the last step's selection
     sel_cnt = prev.sel_cnt.cpu().numpy()
     w_last = w.replace(seq_lens=tuple(lens))      # the lengths of the last timed step
+    compact = None
+    if args.compact:
+        # Per step: each moved block's g key and value rows read and written, plus the slot
+        # rows read and written and the selection read by the planning kernel.
+        mv = hist_moved[args.warmup:].cpu().numpy().astype(np.int64)
+        blk = np.array([2 * 2 * p.block * w.head_dim * w.elem_bytes for p in w.policies])
+        moved_bytes = (mv * blk[None, :]).sum(axis=1) + 3 * w.num_units * plan.max_selected * 4
+        c_ms = np.array([ev_c0[i].elapsed_time(ev_c1[i]) for i in timed])
+        compact = {"us_median": round(float(np.median(c_ms)) * 1e3, 2),
+                   "moved_blocks_per_step_mean": round(float(mv.sum(axis=1).mean()), 1),
+                   "moved_blocks_per_unit_max": int(mv.max()),
+                   "alg_bytes_per_step_mean": int(moved_bytes.mean()),
+                   "achieved": round(float((moved_bytes / (c_ms * 1e-3)).mean() / 1e9), 1),
+                   "unit": "GB/s"}
+        log(f"[bench] compaction: {compact}")
     total_b, dec_b, sd_b, parts = algorithmic_bytes(w_last, plan.max_selected, sel_idx, sel_cnt,
                                                     ed=args.ed)
+    if compact:
+        parts["compaction"] = compact["alg_bytes_per_step_mean"]
+        total_b += compact["alg_bytes_per_step_mean"]
     value = total_b / (ms_per_step * 1e-3) / 1e9
     achieved = dec_b / (dec_avg * 1e-3) / 1e9
     sd_med = float(np.median(phases["select_decode"]))
@@ -391,6 +423,8 @@ def main() -> int:
     }
     if drift:
         line["selection_drift"] = drift
+    if compact:
+        line["compaction"] = compact
     print(json.dumps(line), flush=True)
     return 0
 

@@ -20,7 +20,8 @@ import torch
 __all__ = [
     "FX_F32", "FX_BF16", "FX_RETRIEVAL", "FX_STREAMING", "FX_NOSA",
     "FX_POOL_KEY", "FX_POOL_SCORE_SUM", "FX_POOL_SCORE_MAX", "fx_unit_summary_offset",
-    "FX_ERR_SEQ_LEN", "FX_ERR_SEL_INDEX", "FX_ERR_SEL_COUNT", "FX_ERR_NONFINITE",
+    "FX_ERR_SEQ_LEN", "FX_ERR_SEL_INDEX", "FX_ERR_SEL_COUNT", "FX_ERR_NONFINITE", "FX_ERR_SLOT_MAP",
+    "fx_compact_update", "fx_unit_work_offset", "fx_unit_max_selected", "WorkingSet", "allocate_working_set",
     "FxError", "Plan", "library_path", "load_library",
     "fx_plan_create", "fx_plan_destroy", "fx_build_summaries", "fx_select",
     "fx_sparse_decode", "fx_sparse_decode_ed", "fx_selection_delta", "fx_read_error", "fx_status_string",
@@ -33,6 +34,7 @@ FX_F32, FX_BF16 = 0, 1
 FX_RETRIEVAL, FX_STREAMING, FX_NOSA = 0, 1, 2
 FX_POOL_KEY, FX_POOL_SCORE_SUM, FX_POOL_SCORE_MAX = 0, 1, 2
 FX_ERR_SEQ_LEN, FX_ERR_SEL_INDEX, FX_ERR_SEL_COUNT, FX_ERR_NONFINITE = 1, 2, 4, 8
+FX_ERR_SLOT_MAP = 16
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
@@ -85,6 +87,11 @@ def load_library(path: Optional[str] = None):
         "fx_max_selected": (_I32, [_P]),
         "fx_unit_block_offset": (ctypes.c_int64, [_P, _I32]),
         "fx_unit_summary_offset": (ctypes.c_int64, [_P, _I32]),
+        "fx_work_bytes": (ctypes.c_size_t, [_P]),
+        "fx_unit_work_offset": (ctypes.c_int64, [_P, _I32]),
+        "fx_unit_max_selected": (_I32, [_P, _I32]),
+        "fx_compact_update": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                     _P]),
         "fx_split_tokens": (_I32, [_P]),
         "fx_status_string": (ctypes.c_char_p, [_I32]),
         "fx_read_error": (_I32, [_P, ctypes.POINTER(ctypes.c_uint32)]),
@@ -154,6 +161,7 @@ class Plan:
     max_selected: int
     split_tokens: int
     pooling: int = 0
+    work_bytes: int = 0
 
     @property
     def units(self) -> int:
@@ -201,7 +209,8 @@ def fx_plan_create(batch: int, num_q_heads: int, num_kv_heads: int, head_dim: in
                 summary_bytes=lib.fx_summary_bytes(h), logits_bytes=lib.fx_logits_bytes(h),
                 evict_mask_bytes=lib.fx_evict_mask_bytes(h),
                 workspace_bytes=lib.fx_workspace_bytes(h), max_selected=lib.fx_max_selected(h),
-                split_tokens=lib.fx_split_tokens(h), pooling=pooling)
+                split_tokens=lib.fx_split_tokens(h), pooling=pooling,
+                work_bytes=lib.fx_work_bytes(h))
 
 
 def fx_plan_destroy(plan: Plan) -> None:
@@ -283,6 +292,52 @@ def fx_sparse_decode_ed(plan: Plan, q: torch.Tensor, K: torch.Tensor, V: torch.T
         _ptr(evict_logits, "evict_logits", torch.float32, plan.logits_bytes // 4, optional=True),
         float(softmax_scale), _ptr(out, "out", dt, nq * plan.head_dim),
         _ptr(lse, "lse", torch.float32, nq, optional=True),
+        _ptr(workspace, "workspace", torch.uint8, plan.workspace_bytes), workspace.numel(),
+        _stream(stream)))
+
+
+def fx_unit_max_selected(plan: Plan, unit: int) -> int:
+    """A unit's selection bound, which is also its number of compaction slots."""
+    return int(load_library().fx_unit_max_selected(plan.handle, int(unit)))
+
+
+def fx_unit_work_offset(plan: Plan, unit: int) -> int:
+    """First working-set row of a unit (-1 if out of range)."""
+    return int(load_library().fx_unit_work_offset(plan.handle, int(unit)))
+
+
+@dataclass
+class WorkingSet:
+    """Caller-owned state of fx_compact_update."""
+    slot_map: torch.Tensor     # int32 [units][max_sel], -1 = free
+    work_K: torch.Tensor       # elem [work_rows][d]
+    work_V: torch.Tensor
+    moved_cnt: torch.Tensor    # int32 [units]
+
+
+def allocate_working_set(plan: Plan, device="cuda") -> WorkingSet:
+    """Allocate (with torch) the block-slot working set of a plan, every slot free."""
+    rows = plan.work_bytes // (plan.elem_bytes * plan.head_dim)
+    return WorkingSet(
+        slot_map=torch.full((plan.units, plan.max_selected), -1, dtype=torch.int32, device=device),
+        work_K=torch.zeros((max(rows, 1), plan.head_dim), dtype=plan.torch_dtype, device=device),
+        work_V=torch.zeros((max(rows, 1), plan.head_dim), dtype=plan.torch_dtype, device=device),
+        moved_cnt=torch.zeros(plan.units, dtype=torch.int32, device=device))
+
+
+def fx_compact_update(plan: Plan, K: torch.Tensor, V: torch.Tensor, seq_lens: torch.Tensor,
+                      sel_idx: torch.Tensor, sel_cnt: torch.Tensor, ws: WorkingSet,
+                      workspace: torch.Tensor, stream=None) -> None:
+    dt = plan.torch_dtype
+    n, u = plan.units * plan.max_selected, plan.units
+    _check("fx_compact_update", load_library().fx_compact_update(
+        plan.handle, _ptr(K, "K", dt, _kv_numel(plan)), _ptr(V, "V", dt, _kv_numel(plan)),
+        _ptr(seq_lens, "seq_lens", torch.int32, plan.batch),
+        _ptr(sel_idx, "sel_idx", torch.int32, n), _ptr(sel_cnt, "sel_cnt", torch.int32, u),
+        _ptr(ws.slot_map, "slot_map", torch.int32, n),
+        _ptr(ws.work_K, "work_K", dt, plan.work_bytes // plan.elem_bytes),
+        _ptr(ws.work_V, "work_V", dt, plan.work_bytes // plan.elem_bytes),
+        _ptr(ws.moved_cnt, "moved_cnt", torch.int32, u, optional=True),
         _ptr(workspace, "workspace", torch.uint8, plan.workspace_bytes), workspace.numel(),
         _stream(stream)))
 

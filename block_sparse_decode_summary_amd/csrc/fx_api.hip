@@ -111,7 +111,8 @@ fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_pl
   p->G = desc->num_q_heads / desc->num_kv_heads;
   p->units = units;
   p->host_units.resize(units);
-  int64_t boff = 0, soff = 0, moff = 0, max_sel = 1, max_ncap = 0, max_nfull = 0, work = 0;
+  int64_t boff = 0, soff = 0, woff = 0, moff = 0, max_sel = 1, max_ncap = 0, max_nfull = 0,
+          work = 0;
   for (int u = 0; u < units; ++u) {
     const fx_head_policy& q = pol[u];
     UnitInfo& ui = p->host_units[u];
@@ -135,8 +136,10 @@ fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_pl
     ui.log2r = desc->pooling == FX_POOL_KEY ? 0 : log2i(q.block / q.sub_block);
     ui.reserved = 0;
     ui.sum_off = soff;
+    ui.work_off = woff;
     boff += n_cap;
     soff += n_cap << ui.log2r;
+    woff += ms * q.block;
     moff += ceil_div(n_cap, 32);
     max_sel = std::max(max_sel, ms);
     max_ncap = std::max(max_ncap, n_cap);
@@ -160,6 +163,7 @@ fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_pl
   }
   p->total_blocks = boff;
   p->summary_rows = soff;
+  p->work_rows = woff;
   p->mask_words = moff;
   p->max_sel = (int32_t)max_sel;
   p->max_n_cap = (int32_t)max_ncap;
@@ -194,6 +198,10 @@ fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_pl
   off += align_up(slots * p->G * 8, 256);
   p->ws_seg_off = off;
   off += align_up((size_t)p->decode_grid * 8, 256);
+  p->ws_moves_off = off;
+  off += align_up((size_t)units * p->max_sel * 8, 256);
+  p->ws_move_cnt_off = off;
+  off += align_up((size_t)units * 4, 256);
   p->ws_total = std::max<size_t>(off, 256);
 
   // Device table: units | error word.
@@ -262,6 +270,18 @@ int64_t fx_unit_block_offset(fx_plan_t p, int32_t unit) {
 int64_t fx_unit_summary_offset(fx_plan_t p, int32_t unit) {
   if (!p || unit < 0 || unit >= p->units) return -1;
   return p->host_units[unit].sum_off;
+}
+size_t fx_work_bytes(fx_plan_t p) {
+  if (!p) return 0;
+  return (size_t)p->work_rows * p->desc.head_dim * (p->desc.dtype == FX_BF16 ? 2 : 4);
+}
+int32_t fx_unit_max_selected(fx_plan_t p, int32_t unit) {
+  if (!p || unit < 0 || unit >= p->units) return -1;
+  return p->host_units[unit].max_sel;
+}
+int64_t fx_unit_work_offset(fx_plan_t p, int32_t unit) {
+  if (!p || unit < 0 || unit >= p->units) return -1;
+  return p->host_units[unit].work_off;
 }
 
 const char* fx_status_string(fx_status s) {
@@ -380,6 +400,28 @@ fx_status fx_sparse_decode_ed(fx_plan_t p, const void* q, const void* K, const v
   return sparse_decode(p, q, K, V, seq_lens, sel_idx, sel_cnt,
                        p->any_nosa ? evict_logits : nullptr, softmax_scale, out, lse, workspace,
                        workspace_bytes, stream);
+}
+
+fx_status fx_compact_update(fx_plan_t p, const void* K, const void* V, const int32_t* seq_lens,
+                            const int32_t* sel_idx, const int32_t* sel_cnt, int32_t* slot_map,
+                            void* work_K, void* work_V, int32_t* moved_cnt, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  if (!p || !req(K, 16) || !req(V, 16) || !req(seq_lens, 4) || !req(sel_idx, 4) ||
+      !req(sel_cnt, 4) || !req(slot_map, 4) || !req(work_K, 16) || !req(work_V, 16) ||
+      !opt(moved_cnt, 4) || !req(workspace, 16))
+    return FX_E_INVALID;
+  if (workspace_bytes < p->ws_total) return FX_E_WORKSPACE;
+  if (p->max_sel > fx::kMaxCompactSlots) return FX_E_UNSUPPORTED;
+  try {
+    char* ws = static_cast<char*>(workspace);
+    return hip_status(fx::launch_compact(p, K, V, seq_lens, sel_idx, sel_cnt, slot_map, work_K,
+                                         work_V, moved_cnt,
+                                         reinterpret_cast<int2*>(ws + p->ws_moves_off),
+                                         reinterpret_cast<int32_t*>(ws + p->ws_move_cnt_off),
+                                         stream));
+  } catch (...) {
+    return FX_E_HIP;
+  }
 }
 
 fx_status fx_selection_delta(fx_plan_t p, const int32_t* prev_idx, const int32_t* prev_cnt,

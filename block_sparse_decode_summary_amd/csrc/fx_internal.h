@@ -42,10 +42,12 @@ struct UnitInfo {
   int32_t log2r;       // log2 of the summary rows per block (0 under key-side pooling)
   int32_t reserved;
   int64_t sum_off;     // first summary row of the unit
+  int64_t work_off;    // first row of the unit's compaction slots (max_sel * g rows)
 };
-static_assert(sizeof(UnitInfo) == 80, "UnitInfo layout");
+static_assert(sizeof(UnitInfo) == 88, "UnitInfo layout");
 
 constexpr int kMaxScoreRows = 64;     // summary rows per block under score-side pooling
+constexpr int kMaxCompactSlots = 2048;   // compaction slots per unit (LDS lists)
 
 }  // namespace fx
 
@@ -67,6 +69,7 @@ struct fx_plan {
 
   int64_t total_blocks = 0;
   int64_t summary_rows = 0;      // sum over units of n_cap * r
+  int64_t work_rows = 0;         // sum over units of max_sel * g (compaction slots)
   int64_t mask_words = 0;
   int32_t max_sel = 0;
   int32_t max_n_cap = 0;
@@ -85,6 +88,8 @@ struct fx_plan {
   size_t ws_part_o_off = 0;      // float [decode_grid][2][G][d]   (head, tail pieces)
   size_t ws_part_ml_off = 0;     // float2 [decode_grid][2][G]     (m, l)
   size_t ws_seg_off = 0;         // int2 [decode_grid]             (unit, pieces)
+  size_t ws_moves_off = 0;       // int2 [units][max_sel]          (compaction moves)
+  size_t ws_move_cnt_off = 0;    // int32 [units]
   size_t ws_total = 0;
 };
 
@@ -112,6 +117,10 @@ hipError_t launch_decode(const fx_plan* p, const void* q, const void* K, const v
 // with the eviction-logit term.
 int decode_grid(const fx_plan* p, bool ed);
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
+hipError_t launch_compact(const fx_plan* p, const void* K, const void* V, const int32_t* seq_lens,
+                          const int32_t* sel_idx, const int32_t* sel_cnt, int32_t* slot_map,
+                          void* work_K, void* work_V, int32_t* moved_cnt, int2* moves,
+                          int32_t* move_cnt, hipStream_t stream);
 hipError_t launch_delta(const fx_plan* p, const int32_t* prev_idx, const int32_t* prev_cnt,
                         const int32_t* cur_idx, const int32_t* cur_cnt, int32_t* added,
                         int32_t* added_cnt, int32_t* removed, int32_t* removed_cnt,

@@ -12,6 +12,8 @@
  *   fx_sparse_decode_ed the same with each NOSA block's eviction logit added to its
  *                       tokens' attention logits (exp-delayed eviction scores)
  *   fx_selection_delta  blocks added to / removed from the previous selection
+ *   fx_compact_update   keep the selected full blocks in a block-slot working set,
+ *                       moving only the newly selected ones
  *
  * Sources, cited by page title and section:
  *   [Fluxion-NL] "Technische Samenvatting: Fluxion" (gist.science/nl/paper/2605.07719)
@@ -127,8 +129,10 @@ enum {
   FX_ERR_SEQ_LEN = 1u << 0,        /* a seq_len was outside [0, t_cap]; clamped */
   FX_ERR_SEL_INDEX = 1u << 1,      /* a selection entry was outside [0, n_tot) or not ascending; skipped */
   FX_ERR_SEL_COUNT = 1u << 2,      /* a sel_cnt was outside [0, max_sel]; clamped */
-  FX_ERR_NONFINITE = 1u << 3       /* a non-finite score or eviction logit; ranked lowest
+  FX_ERR_NONFINITE = 1u << 3,      /* a non-finite score or eviction logit; ranked lowest
                                       (fx_sparse_decode_ed: counted as 0) */
+  FX_ERR_SLOT_MAP = 1u << 4        /* fx_compact_update: a slot row held one block twice and
+                                      some selected blocks found no free slot */
 };
 
 typedef struct {
@@ -195,6 +199,10 @@ size_t fx_workspace_bytes(fx_plan_t plan);     /* workspace for fx_select and fx
 int32_t fx_max_selected(fx_plan_t plan);       /* max_sel: row stride of sel_idx and delta lists */
 int64_t fx_unit_block_offset(fx_plan_t plan, int32_t unit);   /* block_off(u), -1 if out of range */
 int64_t fx_unit_summary_offset(fx_plan_t plan, int32_t unit); /* sum_off(u), -1 if out of range */
+size_t fx_work_bytes(fx_plan_t plan);          /* work_rows * d * sizeof(elem): each of work_K, work_V */
+int64_t fx_unit_work_offset(fx_plan_t plan, int32_t unit);    /* work_off(u), -1 if out of range */
+int32_t fx_unit_max_selected(fx_plan_t plan, int32_t unit);   /* max_sel(u): selection bound and
+                                                                 compaction slots, -1 if out of range */
 int32_t fx_split_tokens(fx_plan_t plan);       /* the split_tokens value the plan uses */
 
 const char* fx_status_string(fx_status status);
@@ -300,6 +308,34 @@ fx_status fx_sparse_decode_ed(fx_plan_t plan, const void* q, const void* K, cons
                               const int32_t* sel_cnt, const float* evict_logits,
                               float softmax_scale, void* out, float* lse, void* workspace,
                               size_t workspace_bytes, hipStream_t stream);
+
+/* [NOSA-DE] Methodik §2 (NOSI), bullet "Optimierte Speicherlayout": the cache is held in
+ * minimal block units and blocks are swapped by set difference, with no contiguous
+ * allocation.  Keeps, per unit, a copy of its selected FULL blocks in a working set of
+ * block slots.  Unit u has max_sel(u) slots (its policy's selection bound); slot s holds
+ * rows work_off(u) + s*g .. + g - 1 of work_K and work_V, elem [work_rows][d]
+ * (fx_work_bytes, fx_unit_work_offset; work_off = sum over u' < u of max_sel(u') * g_u').
+ * slot_map int32 [units][max_sel] names the block in each slot (-1 = free); it is
+ * state owned by the caller, set to -1 before the first call, updated in place (entries
+ * past max_sel(u) are not read).  With target = the valid selected blocks j < n_full
+ * (sel_idx / sel_cnt as written by fx_select; the partial last block still grows and is
+ * never held), each call:
+ *   1. frees every slot whose block is not in target;
+ *   2. gives the target blocks no slot holds, in ascending block order, the free slots
+ *      in ascending slot order (held blocks never move);
+ *   3. copies each newly placed block's g key rows and g value rows from K, V into its
+ *      slot (rows of slots that did not change are not touched).
+ * moved_cnt int32 [units] (may be NULL) receives the number of blocks copied per unit.
+ * Needs max_sel <= 2048 (else FX_E_UNSUPPORTED).  workspace as for fx_select (a part of
+ * it that select and decode do not use).  Bad device data: a selection entry that is not
+ * valid is skipped (FX_ERR_SEL_INDEX); more target blocks than slots keeps the lowest
+ * ones (FX_ERR_SEL_COUNT); a slot row naming a block twice can leave blocks without a
+ * slot (FX_ERR_SLOT_MAP).  No access leaves its buffer in any of these cases. */
+fx_status fx_compact_update(fx_plan_t plan, const void* K, const void* V,
+                            const int32_t* seq_lens, const int32_t* sel_idx,
+                            const int32_t* sel_cnt, int32_t* slot_map, void* work_K,
+                            void* work_V, int32_t* moved_cnt, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
 
 /* [NOSA-DE] Methodik §2, bullet "Optimierte Speicherlayout" (set differences of
  * block selections drive block swapping); Methodik §1, "Lokalitätsgarantie".

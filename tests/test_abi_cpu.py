@@ -107,5 +107,8 @@ def test_null_arguments_rejected_on_host(lib):
     assert lib.fx_plan_destroy(None) == 0
     assert lib.fx_unit_block_offset(None, 0) == -1
     assert lib.fx_unit_summary_offset(None, 0) == -1
+    assert lib.fx_unit_work_offset(None, 0) == -1 and lib.fx_unit_max_selected(None, 0) == -1
+    assert lib.fx_work_bytes(None) == 0
+    assert lib.fx_compact_update(None, *([None] * 10), 0, None) == 1
     assert lib.fx_sparse_decode_ed(None, *([None] * 7), ctypes.c_float(1.0), None, None, None, 0,
                                    None) == 1
