@@ -6,7 +6,11 @@ A step is one pass of the whole hot path over one batch of synthetic input:
   fx_select           (scores + per-kv-head selection)
   fx_sparse_decode    (attention over the selected blocks in equal segments + merge)
   fx_selection_delta  (against the previous step's selection)
-Inputs are resident in HBM before timing starts.  The default workload is the mixed
+Inputs are resident in HBM before timing starts.  The timed steps carry events only at
+their boundaries (an event between two kernels delays the second by a few microseconds);
+the decode time, the select + decode time and the phase split are each measured in a
+further pass over the same steps with events around just that part.  The default
+workload is the mixed
 serving batch (64 sequences of U{8192..131072} tokens, 32 q / 8 kv heads, d 128,
 bf16, block 64, streaming/retrieval kv heads), the largest of the five workloads.
 
@@ -228,35 +232,41 @@ def main() -> int:
     cur, prev = A, Bsel
     lens = list(w.seq_lens)
 
-    def step(i):
+    # Events between the kernels of a step delay the next dispatch by a few microseconds,
+    # so the timed loop records events only at step boundaries.  Phase times come from
+    # separate loops over the same steps, each with events only around what it measures.
+    def step(i, ev=None):
+        """One step; ev maps marks ("b1" after the build, "d0" / "d1" around the decode,
+        "c0" / "c1" around the compaction) to per-step event lists."""
         nonlocal cur, prev
+        ev = ev or {}
+        mark = lambda k: ev[k][i].record() if k in ev else None
         q = qs[i % len(qs)]
         fx.fx_build_summaries(plan, inp.K, inp.seq_lens, -1, INT32_MAX, A.summaries)
-        ev_b1[i].record()
+        mark("b1")
         fx.fx_select(plan, q, A.summaries, logits, mask, inp.seq_lens, cur.sel_idx, cur.sel_cnt,
                      A.workspace)
-        ev_d0[i].record()
+        mark("d0")
         if args.ed:
             fx.fx_sparse_decode_ed(plan, q, inp.K, inp.V, inp.seq_lens, cur.sel_idx, cur.sel_cnt,
                                    logits, scale, A.out, A.lse, A.workspace)
         else:
             fx.fx_sparse_decode(plan, q, inp.K, inp.V, inp.seq_lens, cur.sel_idx, cur.sel_cnt,
                                 scale, A.out, A.lse, A.workspace)
-        ev_d1[i].record()
+        mark("d1")
         fx.fx_selection_delta(plan, prev.sel_idx, prev.sel_cnt, cur.sel_idx, cur.sel_cnt,
                               A.added, A.added_cnt, A.removed, A.removed_cnt)
         if wset is not None:
-            ev_c0[i].record()
+            mark("c0")
             fx.fx_compact_update(plan, inp.K, inp.V, inp.seq_lens, cur.sel_idx, cur.sel_cnt, wset,
                                  A.workspace)
-            ev_c1[i].record()
+            mark("c1")
             hist_moved[i].copy_(wset.moved_cnt)
         cur, prev = prev, cur
 
     n_ev = args.warmup + args.steps
     mk = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
-    ev_s0, ev_s1, ev_b1, ev_d0, ev_d1 = mk(), mk(), mk(), mk(), mk()
-    ev_c0, ev_c1 = (mk(), mk()) if args.compact else (None, None)
+    ev_s0, ev_s1 = mk(), mk()
     hist_moved = torch.zeros(n_ev, w.num_units, dtype=torch.int32, device=dev) if args.compact else None
     # Per-step selection statistics of multi-step (drifting query) workloads, copied out
     # after each step's end event.
@@ -288,19 +298,39 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     timed = range(args.warmup, n_ev)
+    moved_main = hist_moved.clone() if args.compact else None   # the later loops overwrite it
     step_ms = [ev_s0[i].elapsed_time(ev_s1[i]) for i in timed]
-    dec_ms = [ev_d0[i].elapsed_time(ev_d1[i]) for i in timed]
+    ms_per_step = float(np.mean(step_ms))
+
+    def marked_loop(marks):
+        """The timed steps again (no token appends), with events at the given marks."""
+        ev = {k: mk() for k in marks}
+        for i in timed:
+            if flush_buf is not None:
+                flush_buf.fill_(i & 0xFF)
+            ev_s0[i].record()
+            step(i, ev)
+            ev_s1[i].record()
+        torch.cuda.synchronize()
+        return ev
+
+    ev = marked_loop(["d0", "d1"])
+    dec_ms = [ev["d0"][i].elapsed_time(ev["d1"][i]) for i in timed]
+    dec_avg = float(np.mean(dec_ms))
+    ev = marked_loop(["b1", "d1"])
+    sd_ms = [ev["b1"][i].elapsed_time(ev["d1"][i]) for i in timed]
+    pm = ["b1", "d0", "d1"] + (["c0", "c1"] if args.compact else [])
+    ev = marked_loop(pm)
     phases = {
-        "build": [ev_s0[i].elapsed_time(ev_b1[i]) for i in timed],
-        "select": [ev_b1[i].elapsed_time(ev_d0[i]) for i in timed],
-        "decode": dec_ms,
-        "delta": [ev_d1[i].elapsed_time(ev_c0[i] if args.compact else ev_s1[i]) for i in timed],
-        "select_decode": [ev_b1[i].elapsed_time(ev_d1[i]) for i in timed],
+        "build": [ev_s0[i].elapsed_time(ev["b1"][i]) for i in timed],
+        "select": [ev["b1"][i].elapsed_time(ev["d0"][i]) for i in timed],
+        "decode": [ev["d0"][i].elapsed_time(ev["d1"][i]) for i in timed],
+        "delta": [ev["d1"][i].elapsed_time(ev["c0"][i] if args.compact else ev_s1[i])
+                  for i in timed],
     }
     if args.compact:
-        phases["compact"] = [ev_c0[i].elapsed_time(ev_c1[i]) for i in timed]
-    ms_per_step = float(np.mean(step_ms))
-    dec_avg = float(np.mean(dec_ms))
+        phases["compact"] = [ev["c0"][i].elapsed_time(ev["c1"][i]) for i in timed]
+    ev_c0, ev_c1 = (ev["c0"], ev["c1"]) if args.compact else (None, None)
     if fx.fx_read_error(plan) != 0:
         raise SystemExit("device error word set during the benchmark")
 
@@ -349,7 +379,7 @@ def main() -> int:
     if args.compact:
         # Per step: each moved block's g key and value rows read and written, plus the slot
         # rows read and written and the selection read by the planning kernel.
-        mv = hist_moved[args.warmup:].cpu().numpy().astype(np.int64)
+        mv = moved_main[args.warmup:].cpu().numpy().astype(np.int64)
         blk = np.array([2 * 2 * p.block * w.head_dim * w.elem_bytes for p in w.policies])
         moved_bytes = (mv * blk[None, :]).sum(axis=1) + 3 * w.num_units * plan.max_selected * 4
         c_ms = np.array([ev_c0[i].elapsed_time(ev_c1[i]) for i in timed])
@@ -367,7 +397,7 @@ def main() -> int:
         total_b += compact["alg_bytes_per_step_mean"]
     value = total_b / (ms_per_step * 1e-3) / 1e9
     achieved = dec_b / (dec_avg * 1e-3) / 1e9
-    sd_med = float(np.median(phases["select_decode"]))
+    sd_med = float(np.median(sd_ms))
     sd_gbs = sd_b / (sd_med * 1e-3) / 1e9
     log(f"[bench] {w.name}: {ms_per_step * 1e3:.1f} us/step (p10 {np.percentile(step_ms, 10) * 1e3:.1f},"
         f" p90 {np.percentile(step_ms, 90) * 1e3:.1f}), decode {dec_avg * 1e3:.1f} us; "
