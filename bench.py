@@ -3,16 +3,18 @@
 
 A step is one pass of the whole hot path over one batch of synthetic input:
   fx_build_summaries  (the newest full block of every unit, as when a block fills)
-  fx_select           (scores + per-kv-head selection)
+  fx_select_delta     (scores + per-kv-head selection + the differences against the
+                       previous step's selection, formed by the selection kernel)
   fx_sparse_decode    (attention over the selected blocks in equal segments + merge)
-  fx_selection_delta  (against the previous step's selection)
+(`--separate-delta`: fx_select, fx_sparse_decode, then fx_selection_delta.)
 Inputs are resident in HBM before timing starts.  The timed steps carry events only at
 their boundaries (an event between two kernels delays the second by a few microseconds);
 the decode time, the select + decode time and the phase split are each measured in a
-further pass over the same steps with events around just that part.  The default
-workload is the mixed
-serving batch (64 sequences of U{8192..131072} tokens, 32 q / 8 kv heads, d 128,
-bf16, block 64, streaming/retrieval kv heads), the largest of the five workloads.
+further pass over the same steps with events around just that part; those passes use
+fx_select and fx_selection_delta as separate calls, so that select + decode is the pair
+fx_select + fx_sparse_decode alone.  The default workload is the mixed serving batch
+(64 sequences of U{8192..131072} tokens, 32 q / 8 kv heads, d 128, bf16, block 64,
+streaming/retrieval kv heads), the largest of the five workloads.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -182,6 +184,8 @@ def main() -> int:
     ap.add_argument("--compact", action="store_true",
                     help="after the delta, keep the selected full blocks in a block-slot working "
                          "set (fx_compact_update), timed as its own phase")
+    ap.add_argument("--separate-delta", action="store_true",
+                    help="fx_select then fx_selection_delta instead of fx_select_delta")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-reference", action="store_true",
@@ -235,6 +239,8 @@ def main() -> int:
     # Events between the kernels of a step delay the next dispatch by a few microseconds,
     # so the timed loop records events only at step boundaries.  Phase times come from
     # separate loops over the same steps, each with events only around what it measures.
+    plain_select = False      # True: fx_select and fx_selection_delta as two calls
+
     def step(i, ev=None):
         """One step; ev maps marks ("b1" after the build, "d0" / "d1" around the decode,
         "c0" / "c1" around the compaction) to per-step event lists."""
@@ -244,8 +250,14 @@ def main() -> int:
         q = qs[i % len(qs)]
         fx.fx_build_summaries(plan, inp.K, inp.seq_lens, -1, INT32_MAX, A.summaries)
         mark("b1")
-        fx.fx_select(plan, q, A.summaries, logits, mask, inp.seq_lens, cur.sel_idx, cur.sel_cnt,
-                     A.workspace)
+        fused = not args.separate_delta and not plain_select
+        if fused:
+            fx.fx_select_delta(plan, q, A.summaries, logits, mask, inp.seq_lens, prev.sel_idx,
+                               prev.sel_cnt, cur.sel_idx, cur.sel_cnt, A.added, A.added_cnt,
+                               A.removed, A.removed_cnt, A.workspace)
+        else:
+            fx.fx_select(plan, q, A.summaries, logits, mask, inp.seq_lens, cur.sel_idx,
+                         cur.sel_cnt, A.workspace)
         mark("d0")
         if args.ed:
             fx.fx_sparse_decode_ed(plan, q, inp.K, inp.V, inp.seq_lens, cur.sel_idx, cur.sel_cnt,
@@ -254,8 +266,9 @@ def main() -> int:
             fx.fx_sparse_decode(plan, q, inp.K, inp.V, inp.seq_lens, cur.sel_idx, cur.sel_cnt,
                                 scale, A.out, A.lse, A.workspace)
         mark("d1")
-        fx.fx_selection_delta(plan, prev.sel_idx, prev.sel_cnt, cur.sel_idx, cur.sel_cnt,
-                              A.added, A.added_cnt, A.removed, A.removed_cnt)
+        if not fused:
+            fx.fx_selection_delta(plan, prev.sel_idx, prev.sel_cnt, cur.sel_idx, cur.sel_cnt,
+                                  A.added, A.added_cnt, A.removed, A.removed_cnt)
         if wset is not None:
             mark("c0")
             fx.fx_compact_update(plan, inp.K, inp.V, inp.seq_lens, cur.sel_idx, cur.sel_cnt, wset,
@@ -302,8 +315,11 @@ def main() -> int:
     step_ms = [ev_s0[i].elapsed_time(ev_s1[i]) for i in timed]
     ms_per_step = float(np.mean(step_ms))
 
-    def marked_loop(marks):
-        """The timed steps again (no token appends), with events at the given marks."""
+    def marked_loop(marks, separate=False):
+        """The timed steps again (no token appends), with events at the given marks;
+        separate: fx_select and fx_selection_delta as two calls."""
+        nonlocal plain_select
+        plain_select = separate
         ev = {k: mk() for k in marks}
         for i in timed:
             if flush_buf is not None:
@@ -312,15 +328,16 @@ def main() -> int:
             step(i, ev)
             ev_s1[i].record()
         torch.cuda.synchronize()
+        plain_select = False
         return ev
 
     ev = marked_loop(["d0", "d1"])
     dec_ms = [ev["d0"][i].elapsed_time(ev["d1"][i]) for i in timed]
     dec_avg = float(np.mean(dec_ms))
-    ev = marked_loop(["b1", "d1"])
+    ev = marked_loop(["b1", "d1"], separate=True)     # fx_select + fx_sparse_decode alone
     sd_ms = [ev["b1"][i].elapsed_time(ev["d1"][i]) for i in timed]
     pm = ["b1", "d0", "d1"] + (["c0", "c1"] if args.compact else [])
-    ev = marked_loop(pm)
+    ev = marked_loop(pm, separate=True)
     phases = {
         "build": [ev_s0[i].elapsed_time(ev["b1"][i]) for i in timed],
         "select": [ev["b1"][i].elapsed_time(ev["d0"][i]) for i in timed],

@@ -24,7 +24,7 @@ __all__ = [
     "fx_compact_update", "fx_unit_work_offset", "fx_unit_max_selected", "WorkingSet", "allocate_working_set",
     "FxError", "Plan", "library_path", "load_library",
     "fx_plan_create", "fx_plan_destroy", "fx_build_summaries", "fx_select",
-    "fx_sparse_decode", "fx_sparse_decode_ed", "fx_selection_delta", "fx_read_error", "fx_status_string",
+    "fx_sparse_decode", "fx_sparse_decode_ed", "fx_selection_delta", "fx_select_delta", "fx_read_error", "fx_status_string",
     "fx_stream_read",
     "StepBuffers", "allocate_step_buffers",
 ]
@@ -102,6 +102,8 @@ def load_library(path: Optional[str] = None):
         "fx_sparse_decode_ed": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
                                        _P, ctypes.c_size_t, _P]),
         "fx_selection_delta": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+        "fx_select_delta": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                   ctypes.c_size_t, _P]),
         "fx_stream_read_sink_words": (ctypes.c_size_t, [ctypes.c_size_t]),
         "fx_stream_read": (_I32, [_P, ctypes.c_size_t, _P, _P]),
     }
@@ -257,6 +259,28 @@ def fx_select(plan: Plan, q: torch.Tensor, summaries: Optional[torch.Tensor],
         _ptr(seq_lens, "seq_lens", torch.int32, plan.batch),
         _ptr(sel_idx, "sel_idx", torch.int32, units * plan.max_selected),
         _ptr(sel_cnt, "sel_cnt", torch.int32, units),
+        _ptr(workspace, "workspace", torch.uint8, plan.workspace_bytes), workspace.numel(),
+        _stream(stream)))
+
+
+def fx_select_delta(plan: Plan, q: torch.Tensor, summaries: Optional[torch.Tensor],
+                    evict_logits: Optional[torch.Tensor], evicted_mask: Optional[torch.Tensor],
+                    seq_lens: torch.Tensor, prev_idx: torch.Tensor, prev_cnt: torch.Tensor,
+                    sel_idx: torch.Tensor, sel_cnt: torch.Tensor, added: torch.Tensor,
+                    added_cnt: torch.Tensor, removed: torch.Tensor, removed_cnt: torch.Tensor,
+                    workspace: torch.Tensor, stream=None) -> None:
+    dt = plan.torch_dtype
+    n, u, i32 = plan.units * plan.max_selected, plan.units, torch.int32
+    _check("fx_select_delta", load_library().fx_select_delta(
+        plan.handle, _ptr(q, "q", dt, plan.batch * plan.num_q_heads * plan.head_dim),
+        _ptr(summaries, "summaries", dt, plan.summary_bytes // plan.elem_bytes, optional=True),
+        _ptr(evict_logits, "evict_logits", torch.float32, plan.logits_bytes // 4, optional=True),
+        _ptr(evicted_mask, "evicted_mask", torch.int32, plan.evict_mask_bytes // 4, optional=True),
+        _ptr(seq_lens, "seq_lens", i32, plan.batch),
+        _ptr(prev_idx, "prev_idx", i32, n), _ptr(prev_cnt, "prev_cnt", i32, u),
+        _ptr(sel_idx, "sel_idx", i32, n), _ptr(sel_cnt, "sel_cnt", i32, u),
+        _ptr(added, "added", i32, n), _ptr(added_cnt, "added_cnt", i32, u),
+        _ptr(removed, "removed", i32, n), _ptr(removed_cnt, "removed_cnt", i32, u),
         _ptr(workspace, "workspace", torch.uint8, plan.workspace_bytes), workspace.numel(),
         _stream(stream)))
 

@@ -330,10 +330,15 @@ fx_status fx_build_summaries(fx_plan_t p, const void* K, const int32_t* seq_lens
   }
 }
 
-fx_status fx_select(fx_plan_t p, const void* q, const void* summaries, const float* evict_logits,
-                    uint32_t* evicted_mask, const int32_t* seq_lens, int32_t* sel_idx,
-                    int32_t* sel_cnt, void* workspace, size_t workspace_bytes,
-                    hipStream_t stream) {
+namespace {
+
+fx_status select_blocks(fx_plan_t p, const void* q, const void* summaries,
+                        const float* evict_logits, uint32_t* evicted_mask,
+                        const int32_t* seq_lens, const int32_t* prev_idx,
+                        const int32_t* prev_cnt, int32_t* sel_idx, int32_t* sel_cnt,
+                        int32_t* added, int32_t* added_cnt, int32_t* removed,
+                        int32_t* removed_cnt, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
   if (!p || !req(q, 16) || !req(seq_lens, 4) || !req(sel_idx, 4) || !req(sel_cnt, 4) ||
       !req(workspace, 16))
     return FX_E_INVALID;
@@ -350,10 +355,37 @@ fx_status fx_select(fx_plan_t p, const void* q, const void* summaries, const flo
     char* ws = static_cast<char*>(workspace);
     return hip_status(fx::launch_topk(p, scores, evict_logits, evicted_mask, seq_lens, sel_idx,
                                       sel_cnt, reinterpret_cast<uint32_t*>(ws + p->ws_keys_off),
-                                      reinterpret_cast<uint32_t*>(ws + p->ws_bits_off), stream));
+                                      reinterpret_cast<uint32_t*>(ws + p->ws_bits_off), prev_idx,
+                                      prev_cnt, added, added_cnt, removed, removed_cnt, stream));
   } catch (...) {
     return FX_E_HIP;
   }
+}
+
+}  // namespace
+
+fx_status fx_select(fx_plan_t p, const void* q, const void* summaries, const float* evict_logits,
+                    uint32_t* evicted_mask, const int32_t* seq_lens, int32_t* sel_idx,
+                    int32_t* sel_cnt, void* workspace, size_t workspace_bytes,
+                    hipStream_t stream) {
+  return select_blocks(p, q, summaries, evict_logits, evicted_mask, seq_lens, nullptr, nullptr,
+                       sel_idx, sel_cnt, nullptr, nullptr, nullptr, nullptr, workspace,
+                       workspace_bytes, stream);
+}
+
+fx_status fx_select_delta(fx_plan_t p, const void* q, const void* summaries,
+                          const float* evict_logits, uint32_t* evicted_mask,
+                          const int32_t* seq_lens, const int32_t* prev_idx,
+                          const int32_t* prev_cnt, int32_t* sel_idx, int32_t* sel_cnt,
+                          int32_t* added, int32_t* added_cnt, int32_t* removed,
+                          int32_t* removed_cnt, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream) {
+  if (!req(prev_idx, 4) || !req(prev_cnt, 4) || !req(added, 4) || !req(added_cnt, 4) ||
+      !req(removed, 4) || !req(removed_cnt, 4) || prev_idx == sel_idx || prev_cnt == sel_cnt)
+    return FX_E_INVALID;
+  return select_blocks(p, q, summaries, evict_logits, evicted_mask, seq_lens, prev_idx,
+                       prev_cnt, sel_idx, sel_cnt, added, added_cnt, removed, removed_cnt,
+                       workspace, workspace_bytes, stream);
 }
 
 namespace {

@@ -101,9 +101,13 @@ hipError_t launch_build_summaries(const fx_plan* p, const void* K, const int32_t
                                   hipStream_t stream);
 hipError_t launch_score(const fx_plan* p, const void* q, const void* summaries,
                         const int32_t* seq_lens, float* scores, hipStream_t stream);
+// prev_idx == nullptr: no delta; else also the differences against prev (fused into
+// the register path, a second kernel on the workspace path).
 hipError_t launch_topk(const fx_plan* p, const float* scores, const float* logits,
                        uint32_t* mask, const int32_t* seq_lens, int32_t* sel_idx,
                        int32_t* sel_cnt, uint32_t* ws_keys, uint32_t* ws_bits,
+                       const int32_t* prev_idx, const int32_t* prev_cnt, int32_t* added,
+                       int32_t* added_cnt, int32_t* removed, int32_t* removed_cnt,
                        hipStream_t stream);
 bool topk_in_registers(const fx_plan* p);   // else keys and bitmaps use the workspace
 // logits == nullptr: plain attention; else each NOSA unit's token of block j also adds

@@ -66,7 +66,8 @@ struct SelectLds {
   uint32_t red[3][NW];
   int scan[2][NW];
   int bcast[3];
-  int rowcnt[kMaxRows * NW];
+  int rowcnt[3][kMaxRows * NW];                 // per list: selection, added, removed
+  uint32_t prevbits[kTopkRegBlocks / 32];       // the previous selection (fused delta)
 };
 
 __device__ __forceinline__ bool bit(const uint32_t* bits, int j) {
@@ -277,12 +278,71 @@ __device__ __forceinline__ uint32_t chosen_bits(const Kth& s, const uint32_t (&k
   return out;
 }
 
+// The set differences against the previous selection, computed by the same workgroup
+// (prev == nullptr: none).  Block j of the unit is bit j / NT of thread j % NT, as for
+// the selection itself.
+struct DeltaArgs {
+  const int32_t* prev_idx;
+  const int32_t* prev_cnt;
+  int32_t* added;
+  int32_t* added_cnt;
+  int32_t* removed;
+  int32_t* removed_cnt;
+};
+
+// Writes the blocks of the per-thread masks m (bit i: block i*NT + t) in ascending order
+// to out[0 .. count), pads out to max_sel with -1 and stores the count.  rowcnt holds,
+// after a barrier, the number of set bits of row i in wave w at rowcnt[i*NW + w].
+template <int KPT>
+__device__ __forceinline__ int write_list(uint32_t m, const int* rowcnt, int32_t* out,
+                                          int max_sel) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  constexpr int NE = KPT * NW;
+  constexpr int R = (NE + 63) / 64;
+  uint32_t excl[R];
+  uint32_t running = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int idx = r * 64 + lane;
+    const uint32_t v = idx < NE ? (uint32_t)rowcnt[idx] : 0u;
+    const uint32_t incl = wave_scan_incl_u32(v);
+    excl[r] = running + incl - v;
+    running += lane_value(incl, 63);
+  }
+  const int total = (int)running;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    // Entries i*NW .. i*NW+NW-1 lie in one 64-entry chunk.
+    const uint64_t b = __ballot((m >> i) & 1u);
+    const int base = (int)lane_value(excl[(i * NW) >> 6], ((i * NW) & 63) + wu);
+    if ((m >> i) & 1u) {
+      const int pos = base + (int)lanes_below(b);
+      if (pos < max_sel) out[pos] = i * NT + t;
+    }
+  }
+  for (int i = min(total, max_sel) + t; i < max_sel; i += NT) out[i] = -1;
+  return total;
+}
+
+template <int KPT>
+__device__ __forceinline__ int row_count(uint32_t m, int i_lane) {
+  int c = 0;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int v = __popcll(__ballot((m >> i) & 1u));
+    c = i_lane == i ? v : c;
+  }
+  return c;
+}
+
 template <int KPT>
 __global__ __launch_bounds__(NT) void k_topk_reg(
     const UnitInfo* __restrict__ units, const float* __restrict__ scores,
     const float* __restrict__ logits, uint32_t* __restrict__ mask,
     const int32_t* __restrict__ seq_lens, int32_t* __restrict__ sel_idx,
-    int32_t* __restrict__ sel_cnt, uint32_t* __restrict__ err, int Hkv, int t_cap, int max_sel) {
+    int32_t* __restrict__ sel_cnt, DeltaArgs D, uint32_t* __restrict__ err, int Hkv, int t_cap,
+    int max_sel) {
   static_assert(KPT <= 32 && KPT * NT <= kTopkRegBlocks, "rows per thread");
   __shared__ SelectLds L;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
@@ -290,6 +350,8 @@ __global__ __launch_bounds__(NT) void k_topk_reg(
     uint4* h = reinterpret_cast<uint4*>(&L.hist[0][8 * t]);
     h[0] = make_uint4(0, 0, 0, 0);
     h[1] = make_uint4(0, 0, 0, 0);
+    if (D.prev_idx)
+      for (int i = t; i < KPT * NT / 32; i += NT) L.prevbits[i] = 0u;
   }
   const int u = blockIdx.x;
   const UnitInfo ui = units[u];
@@ -363,45 +425,58 @@ __global__ __launch_bounds__(NT) void k_topk_reg(
     sel |= ge | chosen_bits(Q, skey, candq);
   }
 
-  // Compact in ascending block order: rows i, then waves w, then lanes.
-  int mycnt = 0;
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const int c = __popcll(__ballot((sel >> i) & 1u));
-    mycnt = lane == i ? c : mycnt;
-  }
-  if (lane < KPT) L.rowcnt[lane * NW + w] = mycnt;
-  __syncthreads();
-  constexpr int NE = KPT * NW;
-  constexpr int R = (NE + 63) / 64;
-  uint32_t excl[R];
-  uint32_t running = 0;
-#pragma unroll
-  for (int r = 0; r < R; ++r) {
-    const int idx = r * 64 + lane;
-    const uint32_t v = idx < NE ? (uint32_t)L.rowcnt[idx] : 0u;
-    const uint32_t incl = wave_scan_incl_u32(v);
-    excl[r] = running + incl - v;
-    running += lane_value(incl, 63);
-  }
-  const int total = (int)running;
-  int32_t* out = sel_idx + (size_t)u * max_sel;
-  const int wu = __builtin_amdgcn_readfirstlane(w);
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    // Entries i*NW .. i*NW+NW-1 lie in one 64-entry chunk.
-    const uint64_t b = __ballot((sel >> i) & 1u);
-    const int base = (int)lane_value(excl[(i * NW) >> 6], ((i * NW) & 63) + wu);
-    if ((sel >> i) & 1u) {
-      const int pos = base + (int)lanes_below(b);
-      if (pos < max_sel) out[pos] = i * NT + t;
+  // The previous selection as a bitmap (the zeroing above is behind a barrier).  Its
+  // entries must be ascending blocks of the unit (as this kernel writes them); others are
+  // skipped and flagged.
+  uint32_t prevm = 0;
+  if (D.prev_idx) {
+    int pc = D.prev_cnt[u];
+    if (pc < 0 || pc > max_sel) {
+      if (t == 0) atomicOr(err, (uint32_t)FX_ERR_SEL_COUNT);
+      pc = min(max(pc, 0), max_sel);
+    }
+    const int32_t* prev = D.prev_idx + (size_t)u * max_sel;
+    for (int i = t; i < pc; i += NT) {
+      const int pj = prev[i];
+      if (pj >= 0 && pj < ui.n_cap && (i == 0 || prev[i - 1] < pj))
+        atomicOr(&L.prevbits[pj >> 5], 1u << (pj & 31));
+      else
+        atomicOr(err, (uint32_t)FX_ERR_SEL_INDEX);
     }
   }
-  const int cnt = min(total, max_sel);
-  for (int i = cnt + t; i < max_sel; i += NT) out[i] = -1;
+
+  // Compact in ascending block order: rows i, then waves w, then lanes.
+  const int c0 = row_count<KPT>(sel, lane);
+  if (lane < KPT) L.rowcnt[0][lane * NW + w] = c0;
+  __syncthreads();   // row counts and the previous-selection bitmap
+  if (D.prev_idx) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int j = i * NT + t;
+      prevm |= ((L.prevbits[j >> 5] >> (j & 31)) & 1u) << i;
+    }
+    const int c1 = row_count<KPT>(sel & ~prevm, lane);
+    const int c2 = row_count<KPT>(prevm & ~sel, lane);
+    if (lane < KPT) {
+      L.rowcnt[1][lane * NW + w] = c1;
+      L.rowcnt[2][lane * NW + w] = c2;
+    }
+  }
+  const int total = write_list<KPT>(sel, L.rowcnt[0], sel_idx + (size_t)u * max_sel, max_sel);
   if (t == 0) {
-    sel_cnt[u] = cnt;
+    sel_cnt[u] = min(total, max_sel);
     if (total > max_sel) atomicOr(err, (uint32_t)FX_ERR_SEL_COUNT);
+  }
+  if (D.prev_idx) {
+    __syncthreads();   // the added / removed row counts
+    const int na = write_list<KPT>(sel & ~prevm, L.rowcnt[1], D.added + (size_t)u * max_sel,
+                                   max_sel);
+    const int nr = write_list<KPT>(prevm & ~sel, L.rowcnt[2], D.removed + (size_t)u * max_sel,
+                                   max_sel);
+    if (t == 0) {
+      D.added_cnt[u] = min(na, max_sel);
+      D.removed_cnt[u] = min(nr, max_sel);
+    }
   }
   if (nonfinite) atomicOr(err, (uint32_t)FX_ERR_NONFINITE);
 }
@@ -545,9 +620,10 @@ __global__ __launch_bounds__(NT) void k_topk_mem(
 
 template <int KPT>
 void launch_reg(const fx_plan* p, const float* scores, const float* logits, uint32_t* mask,
-                const int32_t* seq_lens, int32_t* sel_idx, int32_t* sel_cnt, hipStream_t stream) {
+                const int32_t* seq_lens, int32_t* sel_idx, int32_t* sel_cnt, const DeltaArgs& D,
+                hipStream_t stream) {
   k_topk_reg<KPT><<<dim3((unsigned)p->units), NT, 0, stream>>>(
-      p->d_units, scores, logits, mask, seq_lens, sel_idx, sel_cnt, p->d_error,
+      p->d_units, scores, logits, mask, seq_lens, sel_idx, sel_cnt, D, p->d_error,
       p->desc.num_kv_heads, p->desc.t_cap, p->max_sel);
 }
 
@@ -557,18 +633,27 @@ bool topk_in_registers(const fx_plan* p) { return p->max_n_cap <= kTopkRegBlocks
 
 hipError_t launch_topk(const fx_plan* p, const float* scores, const float* logits, uint32_t* mask,
                        const int32_t* seq_lens, int32_t* sel_idx, int32_t* sel_cnt,
-                       uint32_t* ws_keys, uint32_t* ws_bits, hipStream_t stream) {
+                       uint32_t* ws_keys, uint32_t* ws_bits, const int32_t* prev_idx,
+                       const int32_t* prev_cnt, int32_t* added, int32_t* added_cnt,
+                       int32_t* removed, int32_t* removed_cnt, hipStream_t stream) {
+  const DeltaArgs D{prev_idx, prev_cnt, added, added_cnt, removed, removed_cnt};
   const int n = p->max_n_cap;
-  if (n <= 1 * NT) launch_reg<1>(p, scores, logits, mask, seq_lens, sel_idx, sel_cnt, stream);
-  else if (n <= 2 * NT) launch_reg<2>(p, scores, logits, mask, seq_lens, sel_idx, sel_cnt, stream);
-  else if (n <= 4 * NT) launch_reg<4>(p, scores, logits, mask, seq_lens, sel_idx, sel_cnt, stream);
-  else if (n <= 8 * NT) launch_reg<8>(p, scores, logits, mask, seq_lens, sel_idx, sel_cnt, stream);
-  else if (n <= 16 * NT) launch_reg<16>(p, scores, logits, mask, seq_lens, sel_idx, sel_cnt, stream);
-  else if (n <= 32 * NT) launch_reg<32>(p, scores, logits, mask, seq_lens, sel_idx, sel_cnt, stream);
-  else
+  if (n <= 1 * NT) launch_reg<1>(p, scores, logits, mask, seq_lens, sel_idx, sel_cnt, D, stream);
+  else if (n <= 2 * NT) launch_reg<2>(p, scores, logits, mask, seq_lens, sel_idx, sel_cnt, D, stream);
+  else if (n <= 4 * NT) launch_reg<4>(p, scores, logits, mask, seq_lens, sel_idx, sel_cnt, D, stream);
+  else if (n <= 8 * NT) launch_reg<8>(p, scores, logits, mask, seq_lens, sel_idx, sel_cnt, D, stream);
+  else if (n <= 16 * NT) launch_reg<16>(p, scores, logits, mask, seq_lens, sel_idx, sel_cnt, D, stream);
+  else if (n <= 32 * NT) launch_reg<32>(p, scores, logits, mask, seq_lens, sel_idx, sel_cnt, D, stream);
+  else {
     k_topk_mem<<<dim3((unsigned)p->units), NT, 0, stream>>>(
         p->d_units, scores, logits, mask, seq_lens, sel_idx, sel_cnt, p->d_error, ws_keys, ws_bits,
         p->desc.num_kv_heads, p->desc.t_cap, p->max_sel);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || !prev_idx) return e;
+    // The workspace path leaves the differences to the delta kernel.
+    return launch_delta(p, prev_idx, prev_cnt, sel_idx, sel_cnt, added, added_cnt, removed,
+                        removed_cnt, stream);
+  }
   return hipGetLastError();
 }
 

@@ -12,6 +12,8 @@
  *   fx_sparse_decode_ed the same with each NOSA block's eviction logit added to its
  *                       tokens' attention logits (exp-delayed eviction scores)
  *   fx_selection_delta  blocks added to / removed from the previous selection
+ *   fx_select_delta     fx_select and fx_selection_delta in one call (the differences
+ *                       are formed where the selection is made)
  *   fx_compact_update   keep the selected full blocks in a block-slot working set,
  *                       moving only the newly selected ones
  *
@@ -269,6 +271,20 @@ fx_status fx_select(fx_plan_t plan, const void* q, const void* summaries,
                     const float* evict_logits, uint32_t* evicted_mask,
                     const int32_t* seq_lens, int32_t* sel_idx, int32_t* sel_cnt,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* fx_select followed by fx_selection_delta(prev, the new selection), in one call: for
+ * plans whose units have at most 8192 block slots the differences are formed by the
+ * selection kernel itself (no separate kernel).  Arguments as for the two calls; prev_idx /
+ * prev_cnt must not be sel_idx / sel_cnt.  prev must be a selection as fx_select writes it
+ * for this plan (ascending block indices of the unit): here an entry that is not is
+ * skipped and sets FX_ERR_SEL_INDEX (fx_selection_delta takes any lists). */
+fx_status fx_select_delta(fx_plan_t plan, const void* q, const void* summaries,
+                          const float* evict_logits, uint32_t* evicted_mask,
+                          const int32_t* seq_lens, const int32_t* prev_idx,
+                          const int32_t* prev_cnt, int32_t* sel_idx, int32_t* sel_cnt,
+                          int32_t* added, int32_t* added_cnt, int32_t* removed,
+                          int32_t* removed_cnt, void* workspace, size_t workspace_bytes,
+                          hipStream_t stream);
 
 /* [Fluxion-NL] Probleemstelling item 1 (after top-k selection, attention runs over
  * the selected KV blocks only); [NOSA-DE] Methodik §1, "ED-DMA" (the exponential
