@@ -447,6 +447,7 @@ def main() -> int:
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
         "us_per_step": round(ms_per_step * 1e3, 2),
+        "step_us_p10_p50_p90": [round(float(np.percentile(step_ms, p)) * 1e3, 2) for p in (10, 50, 90)],
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": w.dtype,
         "data": "synthetic (seeded; shapes and value distributions of the workload definition)",
