@@ -161,6 +161,19 @@ def test_group_sizes_and_head_dims(G, d, dtype):
     _run_and_compare_all(w)
 
 
+def test_wide_selection_workgroups():
+    """Few units with thousands of block slots take the 1024-thread selection workgroups:
+    every mode, budgets and NOSA state over two drift steps, against the oracle."""
+    pols = []
+    for _ in range(2):
+        pols += [HeadPolicy(MODE_RETRIEVAL, block=8, sub_block=4, budget=float(np.float32(0.07)),
+                            force_sink=1, force_last=1),
+                 HeadPolicy(MODE_NOSA, block=8, sub_block=8, top_k=37, k_evict=90),
+                 HeadPolicy(MODE_STREAMING, block=8, sub_block=8, sink_tokens=16, local_tokens=300)]
+    w = _custom("wide_select", 2, 6, 3, 64, "bf16", 40000, [40000, 23457], pols)
+    _run_and_compare_all(w.replace(drift=(0.9, 0.44), steps=2), steps=2)
+
+
 def test_split_invariance_and_determinism():
     w = small_workload("qwen7b_layer")
     inp = generate(w, DEV)
