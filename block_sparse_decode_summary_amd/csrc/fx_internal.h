@@ -18,6 +18,8 @@ constexpr int kMaxSplit = 2048;       // largest minimum decode segment; also th
                                       // whose block indices one LDS list holds
 constexpr int kMinSplit = 64;
 constexpr int kAutoSplit = 256;       // minimum decode segment when the caller passes 0
+constexpr int kShortSegment = 1024;   // below this many tokens per segment, use half the grid
+constexpr int kCUsMin = 64;           // (only on grids of at least 2 * kCUsMin workgroups)
 constexpr uint64_t kStreamReadSpan = 1ull << 20;   // bytes per workgroup of fx_stream_read
 constexpr int kMaxTcap = 1 << 24;
 constexpr int kTopkRegBlocks = 8192;   // selection keeps keys in registers up to this n_cap

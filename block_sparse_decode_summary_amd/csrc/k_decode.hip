@@ -18,7 +18,8 @@
 //
 // Work split (stream-K): the units' token ranges, laid end to end in unit order, form
 // one sequence of `total` tokens, cut into equal segments of S = max(ceil(total / P),
-// split) tokens, P being the number of workgroups that fit on the device at once.  The
+// split) tokens, P being the number of workgroups that fit on the device at once (half
+// of them when total / P is below kShortSegment tokens).  The
 // grid has exactly P workgroups, all resident; workgroup s streams segment s, which may
 // cover the end of one unit, whole units, and the start of another.  Every workgroup
 // first scans all units (selected-token count N_u from seq_lens, sel_cnt and the last
@@ -216,7 +217,7 @@ __global__ __launch_bounds__(NT) void k_decode(
   constexpr int STEP = TPW * U;       // tokens per wave per step
   static_assert(LPT >= 4 && LPT <= 32 && 64 % LPT == 0, "lane layout");
   __shared__ DecodeLds<E, D, G, ED> L;
-  const int P = gridDim.x, seg = blockIdx.x;
+  const int seg = blockIdx.x;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
 
@@ -245,6 +246,13 @@ __global__ __launch_bounds__(NT) void k_decode(
 #pragma unroll
   for (int i = 0; i < NWAVES; ++i) total += L.scan[0][i];
   total = __builtin_amdgcn_readfirstlane(total);   // uniform: keep what follows scalar
+  // Segments: one per workgroup of the grid, or, when they would be short, one per
+  // workgroup of its first half (dispatched first, so spread over all CUs); the second
+  // half then exits after the scans.  Fewer, longer segments amortise each workgroup's
+  // fixed costs (scans, first loads, merge) and cut the units into fewer pieces.
+  int P = gridDim.x;
+  if ((total + P - 1) / P < kShortSegment && P >= 2 * kCUsMin) P >>= 1;
+  P = __builtin_amdgcn_readfirstlane(P);
   const int S = max((total + P - 1) / P, split);
   const int nseg = (total + S - 1) / S;
   const int s0 = seg * S, s1 = min(s0 + S, total);
