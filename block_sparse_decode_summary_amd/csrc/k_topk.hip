@@ -29,12 +29,14 @@
 // until at most 64 candidates share it; those are gathered into one wave, which ranks
 // them with lane broadcasts.
 //
-// Mapping: one 256-thread workgroup per unit.  Thread t owns blocks j = i*256 + t.
-// When every unit has at most 32*256 block slots the keys, the candidate flags and the
-// old eviction words stay in registers (k_topk_reg), wave ballots of the per-block
-// flags give the bitmap words, and a scan over (row, wave) counts compacts the
-// selection straight into sel_idx in ascending order.  Larger units keep keys and
-// bitmaps in the workspace (k_topk_mem), with the same selection arithmetic.
+// Mapping: one NT-thread workgroup per unit (NT = 256, or 1024 for plans with few
+// units and more than 1024 block slots).  Thread t owns blocks j = i*NT + t.  When every
+// unit has at most 8192 block slots the keys, the candidate flags and the old eviction
+// words stay in registers (k_topk_reg), wave ballots of the per-block flags give the
+// bitmap words, and a scan over (row, wave) counts compacts the selection straight into
+// sel_idx in ascending order; with a previous selection (fx_select_delta) the added and
+// removed lists are compacted the same way.  Larger units keep keys and bitmaps in the
+// workspace (k_topk_mem, 256 threads), with the same selection arithmetic.
 #include <climits>
 #include <type_traits>
 
