@@ -204,10 +204,14 @@ fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_pl
   off += align_up((size_t)units * 4, 256);
   p->ws_total = std::max<size_t>(off, 256);
 
-  // Device table: units | error word.
+  // Device table: units | error word | scored unit ids | every unit id, scored first.
   const size_t tab_units = align_up(sizeof(UnitInfo) * units, 256);
   p->n_scored = (int32_t)p->host_scored.size();
-  const size_t tab_bytes = tab_units + 256 + align_up(sizeof(int32_t) * p->host_scored.size(), 256);
+  const size_t tab_scored = align_up(sizeof(int32_t) * p->host_scored.size(), 256);
+  const size_t tab_bytes = tab_units + 256 + tab_scored + align_up(sizeof(int32_t) * units, 256);
+  std::vector<int32_t> host_order(p->host_scored);
+  for (int32_t u = 0; u < units; ++u)
+    if (p->host_units[u].mode == FX_STREAMING) host_order.push_back(u);
   if (hipGetDevice(&p->device) != hipSuccess ||
       hipMalloc(&p->d_table, tab_bytes) != hipSuccess) {
     delete p;
@@ -217,7 +221,10 @@ fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_pl
   p->d_units = reinterpret_cast<UnitInfo*>(base);
   p->d_error = reinterpret_cast<uint32_t*>(base + tab_units);
   p->d_scored = reinterpret_cast<int32_t*>(base + tab_units + 256);
+  p->d_order = reinterpret_cast<int32_t*>(base + tab_units + 256 + tab_scored);
   if (hipMemcpy(p->d_units, p->host_units.data(), sizeof(UnitInfo) * units,
+                hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(p->d_order, host_order.data(), sizeof(int32_t) * units,
                 hipMemcpyHostToDevice) != hipSuccess ||
       (p->n_scored > 0 &&
        hipMemcpy(p->d_scored, p->host_scored.data(), sizeof(int32_t) * p->n_scored,
@@ -348,6 +355,11 @@ fx_status select_blocks(fx_plan_t p, const void* q, const void* summaries,
   if (workspace_bytes < p->ws_total) return FX_E_WORKSPACE;
   try {
     float* scores = reinterpret_cast<float*>(static_cast<char*>(workspace) + p->ws_scores_off);
+    if (fx::select_fused(p))
+      return hip_status(fx::launch_select_fused(p, q, summaries, scores, evict_logits,
+                                                evicted_mask, seq_lens, sel_idx, sel_cnt,
+                                                prev_idx, prev_cnt, added, added_cnt, removed,
+                                                removed_cnt, stream));
     if (p->any_scored) {
       hipError_t e = fx::launch_score(p, q, summaries, seq_lens, scores, stream);
       if (e != hipSuccess) return FX_E_HIP;

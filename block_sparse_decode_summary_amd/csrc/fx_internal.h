@@ -23,6 +23,7 @@ constexpr int kCUsMin = 64;           // (only on grids of at least 2 * kCUsMin 
 constexpr uint64_t kStreamReadSpan = 1ull << 20;   // bytes per workgroup of fx_stream_read
 constexpr int kMaxTcap = 1 << 24;
 constexpr int kTopkRegBlocks = 8192;   // selection keeps keys in registers up to this n_cap
+constexpr int kFusedSelectBlocks = 256;   // scores formed inside the selection up to this n_cap
 
 // Per-unit policy as the kernels read it (device table owned by the plan).
 struct UnitInfo {
@@ -60,11 +61,13 @@ struct fx_plan {
   std::vector<fx::UnitInfo> host_units;
   std::vector<int32_t> host_scored;
   int device = 0;
-  // device table: [units] UnitInfo | uint32 error word | [n_scored] int32 unit ids
+  // device table: [units] UnitInfo | uint32 error word | [n_scored] int32 unit ids |
+  // [units] int32 unit ids
   void* d_table = nullptr;
   fx::UnitInfo* d_units = nullptr;
   uint32_t* d_error = nullptr;
   int32_t* d_scored = nullptr;   // retrieval and NOSA units, ascending
+  int32_t* d_order = nullptr;    // every unit: the scored ones, then the others (ascending)
   int32_t n_scored = 0;
   int32_t max_scored_n_full_cap = 0;   // max over scored units of t_cap / g
   int32_t max_scored_rows_cap = 0;     // max over scored units of (t_cap / g) * r
@@ -112,6 +115,14 @@ hipError_t launch_topk(const fx_plan* p, const float* scores, const float* logit
                        int32_t* added_cnt, int32_t* removed, int32_t* removed_cnt,
                        hipStream_t stream);
 bool topk_in_registers(const fx_plan* p);   // else keys and bitmaps use the workspace
+// Scores formed by the selection kernel itself (no k_score launch, no score reload).
+bool select_fused(const fx_plan* p);
+hipError_t launch_select_fused(const fx_plan* p, const void* q, const void* summaries,
+                               float* scores, const float* logits, uint32_t* mask,
+                               const int32_t* seq_lens, int32_t* sel_idx, int32_t* sel_cnt,
+                               const int32_t* prev_idx, const int32_t* prev_cnt, int32_t* added,
+                               int32_t* added_cnt, int32_t* removed, int32_t* removed_cnt,
+                               hipStream_t stream);
 // logits == nullptr: plain attention; else each NOSA unit's token of block j also adds
 // logits[block_off + j] to its attention logit.
 hipError_t launch_decode(const fx_plan* p, const void* q, const void* K, const void* V,

@@ -37,18 +37,10 @@
 // so lane i reading word c of row i never shares a bank with another lane), and the
 // lane's chain continues across the chunks in column order.  Small LDS per workgroup
 // keeps several workgroups, and their loads, resident on each CU.
-#include "fx_device.h"
+#include "fx_score_tile.h"
 
 namespace fx {
 namespace {
-
-__device__ __forceinline__ double elem_f64(const uint32_t* row, int c, float*) {
-  return (double)__uint_as_float(row[c]);
-}
-__device__ __forceinline__ double elem_f64(const uint32_t* row, int c, bf16_t*) {
-  const uint32_t w = row[c >> 1];
-  return (double)((c & 1) ? bf16_hi(w) : bf16_lo(w));
-}
 
 constexpr int kTile = 64;         // summary rows per tile (one per lane)
 constexpr int kWaves = 4;         // tiles per workgroup (one per wave)

@@ -37,10 +37,17 @@
 // sel_idx in ascending order; with a previous selection (fx_select_delta) the added and
 // removed lists are compacted the same way.  Larger units keep keys and bitmaps in the
 // workspace (k_topk_mem, 256 threads), with the same selection arithmetic.
+//
+// Plans whose units have at most 256 block slots and key-side summaries of at most 256
+// bytes per row skip the separate scoring kernel: k_select_fused forms each unit's scores
+// in its own selection workgroup (wave w scores blocks 64w .. 64w+63, each lane one
+// block, into the register the selection reads), with the float64 chain of k_score, so
+// the scores are the same bits.  Larger units keep k_score: one CU streams a unit's
+// summaries far more slowly than the whole GPU scoring its tiles in parallel.
 #include <climits>
 #include <type_traits>
 
-#include "fx_device.h"
+#include "fx_score_tile.h"
 
 namespace fx {
 
@@ -82,7 +89,47 @@ hipError_t dispatch_reg(int n, const DA& D, LaunchReg&& launch) {
   return hipGetLastError();
 }
 
+// Summary element type and head dim of the fused kernel (rows of at most 256 bytes).
+template <class F>
+hipError_t by_element(const fx_plan* p, F&& f) {
+  if (p->desc.dtype == FX_BF16) {
+    if (p->desc.head_dim == 128) f(bf16_t{}, std::integral_constant<int, 128>{});
+    else f(bf16_t{}, std::integral_constant<int, 64>{});
+  } else {
+    f(float{}, std::integral_constant<int, 64>{});
+  }
+  return hipGetLastError();
+}
+
 }  // namespace
+
+// Scores and selection in one kernel: key-side summaries, summary rows of at most 256
+// bytes (a wave's 64-row tile then fits in 64 registers per lane) and at most
+// kFusedSelectBlocks block slots per unit: 256 threads per unit, one 64-block tile per
+// wave.  Larger units keep the separate scoring kernel: one CU cannot stream a large
+// unit's summaries as fast as the whole GPU scoring it tile by tile.
+bool select_fused(const fx_plan* p) {
+  const int row_bytes = p->desc.head_dim * (p->desc.dtype == FX_BF16 ? 2 : 4);
+  return p->any_scored && p->desc.pooling == FX_POOL_KEY && row_bytes <= 256 &&
+         p->max_n_cap <= kFusedSelectBlocks;
+}
+
+hipError_t launch_select_fused(const fx_plan* p, const void* q, const void* summaries,
+                               float* scores, const float* logits, uint32_t* mask,
+                               const int32_t* seq_lens, int32_t* sel_idx, int32_t* sel_cnt,
+                               const int32_t* prev_idx, const int32_t* prev_cnt, int32_t* added,
+                               int32_t* added_cnt, int32_t* removed, int32_t* removed_cnt,
+                               hipStream_t stream) {
+  const int n = p->max_n_cap;
+  if (n <= topk256::NT) {
+    const topk256::DeltaArgs D{prev_idx, prev_cnt, added, added_cnt, removed, removed_cnt};
+    return by_element(p, [&](auto e, auto dim) {
+      topk256::launch_fused<1, decltype(e), decltype(dim)::value>(
+          p, q, summaries, scores, logits, mask, seq_lens, sel_idx, sel_cnt, D, stream);
+    });
+  }
+  return hipErrorInvalidValue;   // select_fused() admits no larger units
+}
 
 hipError_t launch_topk(const fx_plan* p, const float* scores, const float* logits, uint32_t* mask,
                        const int32_t* seq_lens, int32_t* sel_idx, int32_t* sel_cnt,

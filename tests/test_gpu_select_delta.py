@@ -10,8 +10,8 @@ import torch
 
 import block_sparse_decode_summary_amd as fx
 from oracle.delta import selection_delta
-from workloads import (HeadPolicy, MODE_RETRIEVAL, WORKLOAD_NAMES, Workload, generate,
-                       query_at_step, small_workload)
+from workloads import (HeadPolicy, MODE_NOSA, MODE_RETRIEVAL, MODE_STREAMING, WORKLOAD_NAMES,
+                       Workload, generate, query_at_step, small_workload)
 
 from gpu_harness import INT32_MAX, make_plan, oracle_unit, say
 
@@ -103,3 +103,63 @@ def test_select_delta_flags_a_bad_previous_selection():
         fx.fx_select_delta(plan, inp.q, B.summaries, None, None, inp.seq_lens, B.sel_idx,
                            B.sel_cnt, B.sel_idx, B.sel_cnt, B.added, B.added_cnt, B.removed,
                            B.removed_cnt, B.workspace)
+
+
+def test_one_kernel_and_two_kernel_selection_agree():
+    """Units of at most 256 block slots (key-side summaries) take the selection kernel that
+    forms the scores itself; one more block slot takes the scoring kernel followed by the
+    selection kernel.  The same cache, queries and eviction logits through both plans give
+    the same scores, selections, eviction masks and differences, bit for bit."""
+    g, n_small = 16, 256
+    pols = (HeadPolicy(MODE_RETRIEVAL, block=g, sub_block=g, top_k=12, force_sink=1, force_last=1),
+            HeadPolicy(MODE_NOSA, block=g, sub_block=g, top_k=8, k_evict=24),
+            HeadPolicy(MODE_STREAMING, block=g, sub_block=g, sink_tokens=16, local_tokens=64),
+            HeadPolicy(MODE_RETRIEVAL, block=g, sub_block=g, budget=0.05, force_sink=1,
+                       force_last=1))
+    wB = Workload(name="one_vs_two_kernels", batch=3, num_q_heads=8, num_kv_heads=4,
+                  head_dim=128, dtype="bf16", t_cap=n_small * g + g,
+                  seq_lens=(n_small * g, 2000, 3001), policies=pols * 3, seed=91,
+                  sink_scaled_tokens=4, needles_per_head=2, steps=4, drift=(0.9, 0.44))
+    wA = wB.replace(t_cap=n_small * g)
+    say(f"[select one/two kernels] units={wB.num_units} n_cap {n_small} and {n_small + 1}")
+    inp = generate(wB, DEV)
+    KA = inp.K[:, :, :wA.t_cap].contiguous()
+    offA, offB = wA.block_offsets(), wB.block_offsets()
+    logitsA = torch.cat([inp.logits[int(offB[u]):int(offB[u]) + wA.n_cap(u)]
+                         for u in range(wA.num_units)])
+    plans = [make_plan(wA), make_plan(wB)]
+    bufs = [fx.allocate_step_buffers(p, DEV) for p in plans]
+    fx.fx_build_summaries(plans[0], KA, inp.seq_lens, 0, INT32_MAX, bufs[0].summaries)
+    fx.fx_build_summaries(plans[1], inp.K, inp.seq_lens, 0, INT32_MAX, bufs[1].summaries)
+    masks = [w.mask_word_offsets() for w in (wA, wB)]
+    for t in range(wB.steps):
+        q = query_at_step(wB, t, DEV) if t > 0 else inp.q
+        for p, X, lg in zip(plans, bufs, (logitsA, inp.logits)):
+            X.prev_idx.copy_(X.sel_idx)
+            X.prev_cnt.copy_(X.sel_cnt)
+            fx.fx_select_delta(p, q, X.summaries, lg, X.evicted_mask, inp.seq_lens, X.prev_idx,
+                               X.prev_cnt, X.sel_idx, X.sel_cnt, X.added, X.added_cnt,
+                               X.removed, X.removed_cnt, X.workspace)
+        torch.cuda.synchronize()
+        A, B = bufs
+        for u in range(wB.num_units):
+            T = wB.seq_lens[u // wB.num_kv_heads]
+            n_full = T // g
+            for name in ("sel", "added", "removed"):
+                idx = getattr(A, "sel_idx" if name == "sel" else name)
+                cnt = getattr(A, "sel_cnt" if name == "sel" else name + "_cnt")
+                idxB = getattr(B, "sel_idx" if name == "sel" else name)
+                cntB = getattr(B, "sel_cnt" if name == "sel" else name + "_cnt")
+                c = int(cnt[u])
+                assert c == int(cntB[u]), f"step {t} unit {u}: {name} count"
+                assert torch.equal(idx[u, :c], idxB[u, :c]), f"step {t} unit {u}: {name}"
+            if pols[u % 4].mode != MODE_STREAMING:
+                sA = A.workspace[int(offA[u]) * 4:(int(offA[u]) + n_full) * 4].view(torch.int32)
+                sB = B.workspace[int(offB[u]) * 4:(int(offB[u]) + n_full) * 4].view(torch.int32)
+                assert torch.equal(sA, sB), f"step {t} unit {u}: scores"
+            mA = A.evicted_mask[int(masks[0][u]):int(masks[0][u + 1])]
+            mB = B.evicted_mask[int(masks[1][u]):int(masks[1][u]) + len(mA)]
+            assert torch.equal(mA, mB), f"step {t} unit {u}: eviction mask"
+    for p in plans:
+        assert fx.fx_read_error(p) == 0
+    say("[select one/two kernels] ok")
