@@ -34,6 +34,25 @@ constexpr int kScoreChunkWords = 32;   // row words staged in LDS at a time
 
 typedef uint32_t ScoreStage[kScoreTile][kScoreChunkWords + 1];
 
+// qs[c] = ((q_0[c] + q_1[c]) + ...) + q_{G-1}[c] in float64 for the G query rows at
+// qgroup (16-byte aligned, rows D elements apart): each of the first G * D * sizeof(E) / 16
+// threads loads 16 bytes into `rows` (one load each, all in flight together), then the
+// first D threads sum a column each.  Every thread of the workgroup calls this; qs is
+// ready after the caller's next barrier.
+template <typename E, int D>
+__device__ __forceinline__ void group_sum_f64(const E* qgroup, int G, uint4* rows, double* qs) {
+  constexpr int QV4 = D * (int)sizeof(E) / 16;
+  const int t = threadIdx.x;
+  if (t < G * QV4) rows[t] = reinterpret_cast<const uint4*>(qgroup)[t];
+  __syncthreads();
+  if (t < D) {
+    const E* qe = reinterpret_cast<const E*>(rows);
+    double a = (double)to_f32(qe[t]);
+    for (int g = 1; g < G; ++g) a = a + (double)to_f32(qe[g * D + t]);
+    qs[t] = a;
+  }
+}
+
 // LDS written by the lanes of a wave is read by other lanes of the same wave: the
 // wave's LDS operations complete in order, and the fences keep the compiler from
 // moving the reads above the writes.
@@ -68,7 +87,10 @@ struct ScoreTile {
       }
   }
 
-  // The float64 chain of row j0 + lane against qs (D doubles in LDS).
+  // The float64 chain of row j0 + lane against qs (D doubles in LDS).  BLOCK: every
+  // wave of the workgroup calls this together and the staging steps use workgroup
+  // barriers; else only wave-level ordering.
+  template <bool BLOCK = false>
   __device__ __forceinline__ double chain(const double* qs, ScoreStage& stage, int lane) const {
     double acc = 0.0;
 #pragma unroll
@@ -82,7 +104,8 @@ struct ScoreTile {
         dst[2] = buf[ch][k].z;
         dst[3] = buf[ch][k].w;
       }
-      wave_lds_sync();
+      if constexpr (BLOCK) __syncthreads();
+      else wave_lds_sync();
       const uint32_t* row = stage[lane];
       {
 #pragma clang fp contract(off)
@@ -93,7 +116,8 @@ struct ScoreTile {
           acc = acc + prod;
         }
       }
-      wave_lds_sync();   // the next chunk overwrites the tile
+      if constexpr (BLOCK) __syncthreads();   // the next chunk overwrites the tile
+      else wave_lds_sync();
     }
     return acc;
   }

@@ -50,10 +50,10 @@ constexpr int kChunkWords = 32;   // row words staged in LDS at a time
 __device__ __forceinline__ double max_nan(double a, double b) { return (a != a || a >= b) ? a : b; }
 __device__ __forceinline__ float max_nan(float a, float b) { return (a != a || a >= b) ? a : b; }
 
-// GM = 0: the group's rows are summed (G is a runtime value); GM = 1..8: the group of
-// GM rows is aggregated by a max.
+// The group-max score (score-side pooling with FX_POOL_SCORE_MAX): G = GM query rows,
+// each with its own chain, aggregated by a max.
 template <typename E, int D, int GM>
-__global__ __launch_bounds__(kWaves * 64) void k_score(
+__global__ __launch_bounds__(kWaves * 64) void k_score_max(
     const UnitInfo* __restrict__ units, const int32_t* __restrict__ scored,
     const E* __restrict__ q, const E* __restrict__ S, const int32_t* __restrict__ seq_lens,
     float* __restrict__ scores, uint32_t* __restrict__ err, int Hkv, int G, int t_cap,
@@ -83,7 +83,8 @@ __global__ __launch_bounds__(kWaves * 64) void k_score(
 
   __shared__ uint32_t rows[kWaves][kTile][kChunkWords + 1];
   __shared__ uint4 qrows[kMaxGroup * QV4];
-  constexpr int NV = GM == 0 ? 1 : GM;          // query vectors of the chains
+  static_assert(GM >= 1 && GM <= kMaxGroup, "group rows");
+  constexpr int NV = GM;                        // query vectors of the chains
   __shared__ double qs[NV * D];
 
   // The whole tile, chunk by chunk: piece m = lane + 64k of chunk ch is row m / CPIECES,
@@ -109,14 +110,8 @@ __global__ __launch_bounds__(kWaves * 64) void k_score(
   const E* qe = reinterpret_cast<const E*>(qrows);
   if ((int)threadIdx.x < D) {
     const int c = threadIdx.x;
-    if constexpr (GM == 0) {
-      double a = (double)to_f32(qe[c]);
-      for (int g = 1; g < G; ++g) a = a + (double)to_f32(qe[g * D + c]);
-      qs[c] = a;
-    } else {
 #pragma unroll
-      for (int g = 0; g < GM; ++g) qs[g * D + c] = (double)to_f32(qe[g * D + c]);
-    }
+    for (int g = 0; g < GM; ++g) qs[g * D + c] = (double)to_f32(qe[g * D + c]);
   }
 
   double acc[NV];
@@ -159,6 +154,61 @@ __global__ __launch_bounds__(kWaves * 64) void k_score(
     scores[(size_t)ui.block_off + (row >> log2r)] = f;
 }
 
+// The group-sum score (key-side summaries, or score-side pooling with the group summed):
+// the float64 chain of fx_score_tile.h, which the selection kernel that forms its own
+// scores shares, so both give the same bits.  A workgroup takes four consecutive tiles of
+// one unit, one per wave; the staging steps use workgroup barriers (measured faster here
+// than per-wave ordering, and than two tiles per wave with the next one in flight).
+template <typename E, int D>
+__global__ __launch_bounds__(kWaves * 64) void k_score_sum(
+    const UnitInfo* __restrict__ units, const int32_t* __restrict__ scored,
+    const E* __restrict__ q, const E* __restrict__ S, const int32_t* __restrict__ seq_lens,
+    float* __restrict__ scores, uint32_t* __restrict__ err, int Hkv, int G, int t_cap,
+    int quads_per_unit) {
+  using Tile = ScoreTile<E, D>;
+  __shared__ ScoreStage stage[kWaves];
+  __shared__ uint4 qrows[kMaxGroup * D * sizeof(E) / 16];
+  __shared__ double qs[D];
+  const int n_su = gridDim.x / quads_per_unit;
+  const int quad = blockIdx.x / n_su;
+  const int su = blockIdx.x % n_su;
+  const int u = scored[su];
+  const UnitInfo ui = units[u];
+  const int b = u / Hkv, h = u % Hkv;
+  const int T = load_seq_len(seq_lens, b, t_cap, err);
+  const int log2r = ui.log2r;
+  const int n_rows = (T >> ui.log2g) << log2r;
+  const int tile0 = quad * kWaves;
+  if (tile0 * kTile >= n_rows) return;
+  const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int j0 = (tile0 + w) * kTile;
+  // Rows past the unit's end read zero without a memory access.
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(S + (size_t)ui.sum_off * D), 0, n_rows * Tile::ROW_BYTES, kRsrcWord3);
+  Tile tile;
+  tile.load(rs, j0, lane);
+  group_sum_f64<E, D>(q + ((size_t)b * Hkv * G + (size_t)h * G) * D, G, qrows, qs);
+  __syncthreads();
+  float f = (float)tile.template chain<true>(qs, stage[w], lane);
+  for (int off = 1; off < (1 << log2r); off <<= 1) f = max_nan(f, __shfl_xor(f, off));
+  const int row = j0 + lane;
+  if ((lane & ((1 << log2r) - 1)) == 0 && row < n_rows)
+    scores[(size_t)ui.block_off + (row >> log2r)] = f;
+}
+
+template <typename E, int D>
+hipError_t launch_sum(const fx_plan* p, const void* q, const void* S, const int32_t* seq_lens,
+                      float* scores, hipStream_t stream) {
+  const int tiles = (p->max_scored_rows_cap + kTile - 1) / kTile;
+  const int quads = (tiles + kWaves - 1) / kWaves;
+  if (quads == 0 || p->n_scored == 0) return hipSuccess;
+  const dim3 grid((unsigned)((int64_t)quads * p->n_scored));
+  k_score_sum<E, D><<<grid, kWaves * 64, 0, stream>>>(
+      p->d_units, p->d_scored, static_cast<const E*>(q), static_cast<const E*>(S), seq_lens,
+      scores, p->d_error, p->desc.num_kv_heads, p->G, p->desc.t_cap, quads);
+  return hipGetLastError();
+}
+
 template <typename E, int D, int GM>
 hipError_t launch_gm(const fx_plan* p, const void* q, const void* S, const int32_t* seq_lens,
                      float* scores, hipStream_t stream) {
@@ -166,7 +216,7 @@ hipError_t launch_gm(const fx_plan* p, const void* q, const void* S, const int32
   const int quads = (tiles + kWaves - 1) / kWaves;
   if (quads == 0 || p->n_scored == 0) return hipSuccess;
   const dim3 grid((unsigned)((int64_t)quads * p->n_scored));
-  k_score<E, D, GM><<<grid, kWaves * 64, 0, stream>>>(
+  k_score_max<E, D, GM><<<grid, kWaves * 64, 0, stream>>>(
       p->d_units, p->d_scored, static_cast<const E*>(q), static_cast<const E*>(S), seq_lens,
       scores, p->d_error, p->desc.num_kv_heads, p->G, p->desc.t_cap, quads);
   return hipGetLastError();
@@ -176,7 +226,7 @@ template <typename E, int D>
 hipError_t launch_t(const fx_plan* p, const void* q, const void* S, const int32_t* seq_lens,
                     float* scores, hipStream_t stream) {
   if (p->desc.pooling != FX_POOL_SCORE_MAX)
-    return launch_gm<E, D, 0>(p, q, S, seq_lens, scores, stream);
+    return launch_sum<E, D>(p, q, S, seq_lens, scores, stream);
   switch (p->G) {
     case 1: return launch_gm<E, D, 1>(p, q, S, seq_lens, scores, stream);
     case 2: return launch_gm<E, D, 2>(p, q, S, seq_lens, scores, stream);
