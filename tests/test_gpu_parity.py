@@ -148,6 +148,9 @@ def test_ragged_degenerate_lengths_and_mixed_modes():
     _run_and_compare_all(w, steps=1)
     for split in (64, 2048):
         _run_and_compare_all(w.replace(name=f"ragged_mixed_s{split}"), split_tokens=split)
+    # 257 block slots per unit: scores from the separate scoring kernel instead of the
+    # selection kernel's own.
+    _run_and_compare_all(w.replace(name="ragged_mixed_two_kernel", t_cap=257 * 16), steps=1)
 
 
 @pytest.mark.parametrize("G,d,dtype", [(1, 128, "bf16"), (3, 128, "bf16"), (8, 128, "bf16"),
@@ -375,10 +378,13 @@ def test_selection_delta_random_lists():
         assert list(bufs.removed[u, :bufs.removed_cnt[u]].cpu()) == list(rr)
 
 
-def test_bad_device_data_is_flagged_not_faulting():
+@pytest.mark.parametrize("t_cap_blocks", [64, 320])
+def test_bad_device_data_is_flagged_not_faulting(t_cap_blocks):
     """seq_len beyond t_cap and out-of-range selection entries are clamped / skipped by the
-    kernels' own checks and reported in the error word."""
+    kernels' own checks and reported in the error word (64 block slots: the selection
+    forms its own scores; 320: the separate scoring kernel)."""
     w = small_workload("tiny")
+    w = w.replace(t_cap=t_cap_blocks * w.policies[0].block)
     inp = generate(w, DEV)
     plan = make_plan(w)
     bufs = fx.allocate_step_buffers(plan, DEV)
