@@ -202,8 +202,11 @@ __device__ __forceinline__ void write_empty_unit(E* out, float* lse, int u, int 
   }
 }
 
+// At least two waves per SIMD: without the bound the G = 8 instantiation takes 254
+// registers and runs at one wave per SIMD (4 registers now spill; the mixed serving batch
+// with 64 query heads decodes in 202 us instead of 238 us).  Smaller groups already fit.
 template <typename E, int D, int G, int U, bool ED>
-__global__ __launch_bounds__(NT) void k_decode(
+__global__ __launch_bounds__(NT, 2) void k_decode(
     const UnitInfo* __restrict__ units, const E* __restrict__ q, const E* __restrict__ K,
     const E* __restrict__ V, const int32_t* __restrict__ seq_lens,
     const int32_t* __restrict__ sel_idx, const int32_t* __restrict__ sel_cnt,
