@@ -18,9 +18,10 @@
 //
 // Work split (stream-K): the units' token ranges, laid end to end in unit order, form
 // one sequence of `total` tokens, cut into equal segments of S = max(ceil(total / P),
-// split) tokens, P being the number of workgroups that fit on the device at once (half
-// of them when total / P is below kShortSegment tokens).  The
-// grid has exactly P workgroups, all resident; workgroup s streams segment s, which may
+// split) tokens, P being the number of workgroups that fit on the device at once, or half
+// of them when total / P is below kShortSegment tokens or when the half grid's segments
+// cut no unit and the full grid's would.  The grid holds the resident
+// workgroups; workgroup s streams segment s, which may
 // cover the end of one unit, whole units, and the start of another.  Every workgroup
 // first scans all units (selected-token count N_u from seq_lens, sel_cnt and the last
 // selected block) for the prefix sums; that costs a few dependent loads once per
@@ -29,7 +30,7 @@
 // that workgroup.  A unit that crosses segment boundaries leaves one partial (o, m, l)
 // per segment it touches: in its first segment in slot 1 ("tail") of that segment, in
 // later ones in slot 0 ("head"); its first segment also records (unit, piece count).
-// Units with no tokens (N_u = 0) get out = 0 and lse = -inf from workgroup u mod P.
+// Units with no tokens (N_u = 0) get out = 0 and lse = -inf from workgroup u mod (grid size).
 //
 // k_decode (4 waves per workgroup): within a piece of a unit, tokens go through LDS
 // lists of at most kMaxSplit tokens' block indices; each list is shared out to the four
@@ -169,7 +170,8 @@ struct DecodeLds {
   float m[NWAVES][G];
   float l[NWAVES][G];
   int scan[2][NWAVES];
-  int first_unit, first_pos;
+  int first_unit, first_pos;       // the unit holding the segment's first token (full grid)
+  int first_unit_h, first_pos_h;   // the same on the half grid
 };
 
 constexpr int kScanKeep = 4;       // unit chunks (NT units each) kept in registers between scans
@@ -249,18 +251,25 @@ __global__ __launch_bounds__(NT, 2) void k_decode(
 #pragma unroll
   for (int i = 0; i < NWAVES; ++i) total += L.scan[0][i];
   total = __builtin_amdgcn_readfirstlane(total);   // uniform: keep what follows scalar
-  // Segments: one per workgroup of the grid, or, when they would be short, one per
-  // workgroup of its first half (dispatched first, so spread over all CUs); the second
-  // half then exits after the scans.  Fewer, longer segments amortise each workgroup's
-  // fixed costs (scans, first loads, merge) and cut the units into fewer pieces.
-  int P = gridDim.x;
-  if ((total + P - 1) / P < kShortSegment && P >= 2 * kCUsMin) P >>= 1;
-  P = __builtin_amdgcn_readfirstlane(P);
-  const int S = max((total + P - 1) / P, split);
-  const int nseg = (total + S - 1) / S;
-  const int s0 = seg * S, s1 = min(s0 + S, total);
+  // Segments: one per workgroup of the grid, or one per workgroup of its first half
+  // (dispatched first, so spread over all CUs; the second half exits after the scans)
+  // when the full grid's segments would be short, or when the half grid's segments cut
+  // no unit while the full grid's cut some (units of equal length, e.g. NOSA heads with a
+  // fixed number of blocks: the merge of their pieces then disappears).  Fewer, longer
+  // segments amortise each workgroup's fixed costs (scans, first loads, merge).
+  const int Pf = gridDim.x;
+  const bool can_half = Pf >= 2 * kCUsMin;
+  const int Ph = can_half ? Pf >> 1 : Pf;
+  const bool short_full = can_half && (total + Pf - 1) / Pf < kShortSegment;
+  const int Sf = max((total + Pf - 1) / Pf, split);
+  const int Sh = max((total + Ph - 1) / Ph, split);
+  // (clamped: a workgroup past the last segment has no first token)
+  const int s0f = (int)min((int64_t)seg * Sf, (int64_t)total);
+  const int s0h = (int)min((int64_t)seg * Sh, (int64_t)total);
 
-  // ---- Scan 2: prefix sums; the unit holding token s0; units without tokens.
+  // ---- Scan 2: prefix sums; the unit holding the segment's first token on either grid;
+  // whether either grid cuts a unit; units without tokens.
+  bool cut_f = false, cut_h = false;
   int running = 0, it = 0;
   for (int c0 = 0; c0 < n_units; c0 += NT, ++it) {
     const int u = c0 + (int)threadIdx.x;
@@ -274,13 +283,27 @@ __global__ __launch_bounds__(NT, 2) void k_decode(
     int chunk_total;
     const int incl = running + block_incl_scan(N, L.scan[(it + 1) & 1], &chunk_total);
     const int excl = incl - N;
-    if (N > 0 && excl <= s0 && s0 < incl) {
+    if (N > 0 && excl <= s0f && s0f < incl) {
       L.first_unit = u;
       L.first_pos = excl;
     }
-    if (u < n_units && N == 0 && u % P == seg) write_empty_unit<E, D>(out, lse, u, Hkv, G);
+    if (N > 0 && excl <= s0h && s0h < incl) {
+      L.first_unit_h = u;
+      L.first_pos_h = excl;
+    }
+    if (N > 0) {
+      cut_f |= excl / Sf != (incl - 1) / Sf;
+      cut_h |= excl / Sh != (incl - 1) / Sh;
+    }
+    if (u < n_units && N == 0 && u % Pf == seg) write_empty_unit<E, D>(out, lse, u, Hkv, G);
     running += chunk_total;
   }
+  cut_f = __syncthreads_or(cut_f);
+  cut_h = __syncthreads_or(cut_h);
+  const bool half = short_full || (can_half && cut_f && !cut_h);
+  const int S = half ? Sh : Sf;
+  const int nseg = (total + S - 1) / S;
+  const int s0 = half ? s0h : s0f, s1 = min(s0 + S, total);
   if (seg >= nseg) {
     if (threadIdx.x == 0) seg_rec[seg] = make_int2(-1, 0);
     return;
@@ -291,8 +314,8 @@ __global__ __launch_bounds__(NT, 2) void k_decode(
   const int lg = lane / LPT, li = lane % LPT;
   constexpr uint32_t kRowBytes = D * sizeof(E);
   bool recorded = false;
-  int u = __builtin_amdgcn_readfirstlane(L.first_unit);
-  int Pu = __builtin_amdgcn_readfirstlane(L.first_pos);
+  int u = __builtin_amdgcn_readfirstlane(half ? L.first_unit_h : L.first_unit);
+  int Pu = __builtin_amdgcn_readfirstlane(half ? L.first_pos_h : L.first_pos);
   int cur = s0;
   while (cur < s1) {
     const UnitTokens ut =
