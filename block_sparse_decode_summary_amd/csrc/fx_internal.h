@@ -23,7 +23,7 @@ constexpr int kCUsMin = 64;           // (only on grids of at least 2 * kCUsMin 
 constexpr uint64_t kStreamReadSpan = 1ull << 20;   // bytes per workgroup of fx_stream_read
 constexpr int kMaxTcap = 1 << 24;
 constexpr int kTopkRegBlocks = 8192;   // selection keeps keys in registers up to this n_cap
-constexpr int kFusedSelectBlocks = 256;   // scores formed inside the selection up to this n_cap
+constexpr int kFusedSelectBlocks = 512;   // scores formed inside the selection up to this n_cap
 
 // Per-unit policy as the kernels read it (device table owned by the plan).
 struct UnitInfo {

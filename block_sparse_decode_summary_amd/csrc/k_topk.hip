@@ -38,7 +38,7 @@
 // removed lists are compacted the same way.  Larger units keep keys and bitmaps in the
 // workspace (k_topk_mem, 256 threads), with the same selection arithmetic.
 //
-// Plans whose units have at most 256 block slots and key-side summaries of at most 256
+// Plans whose units have at most 512 block slots and key-side summaries of at most 256
 // bytes per row skip the separate scoring kernel: k_select_fused forms each unit's scores
 // in its own selection workgroup (wave w scores blocks 64w .. 64w+63, each lane one
 // block, into the register the selection reads), with the float64 chain of k_score, so
@@ -58,6 +58,15 @@ constexpr int NT = 256;
 #include "k_topk_body.inc"
 #undef FX_TOPK_WORKSPACE_PATH
 }  // namespace topk256
+
+// 512 threads per unit: the selection that forms its own scores for units of 257-512 block
+// slots (one 64-block tile per wave).
+namespace topk512 {
+constexpr int NT = 512;
+#define FX_TOPK_WORKSPACE_PATH 0
+#include "k_topk_body.inc"
+#undef FX_TOPK_WORKSPACE_PATH
+}  // namespace topk512
 
 // 1024 threads per unit: plans with few units, whose selections would otherwise run on a
 // few CUs with many blocks per thread.
@@ -105,9 +114,10 @@ hipError_t by_element(const fx_plan* p, F&& f) {
 
 // Scores and selection in one kernel: key-side summaries, summary rows of at most 256
 // bytes (a wave's 64-row tile then fits in 64 registers per lane) and at most
-// kFusedSelectBlocks block slots per unit: 256 threads per unit, one 64-block tile per
-// wave.  Larger units keep the separate scoring kernel: one CU cannot stream a large
-// unit's summaries as fast as the whole GPU scoring it tile by tile.
+// kFusedSelectBlocks block slots per unit: one 64-block tile per wave, 256 threads per
+// unit up to 256 block slots, else 512.  Larger units keep the separate scoring kernel:
+// one CU cannot stream a large unit's summaries as fast as the whole GPU scoring it tile
+// by tile.
 bool select_fused(const fx_plan* p) {
   const int row_bytes = p->desc.head_dim * (p->desc.dtype == FX_BF16 ? 2 : 4);
   return p->any_scored && p->desc.pooling == FX_POOL_KEY && row_bytes <= 256 &&
@@ -125,6 +135,13 @@ hipError_t launch_select_fused(const fx_plan* p, const void* q, const void* summ
     const topk256::DeltaArgs D{prev_idx, prev_cnt, added, added_cnt, removed, removed_cnt};
     return by_element(p, [&](auto e, auto dim) {
       topk256::launch_fused<1, decltype(e), decltype(dim)::value>(
+          p, q, summaries, scores, logits, mask, seq_lens, sel_idx, sel_cnt, D, stream);
+    });
+  }
+  if (n <= topk512::NT) {
+    const topk512::DeltaArgs D{prev_idx, prev_cnt, added, added_cnt, removed, removed_cnt};
+    return by_element(p, [&](auto e, auto dim) {
+      topk512::launch_fused<1, decltype(e), decltype(dim)::value>(
           p, q, summaries, scores, logits, mask, seq_lens, sel_idx, sel_cnt, D, stream);
     });
   }

@@ -148,9 +148,10 @@ def test_ragged_degenerate_lengths_and_mixed_modes():
     _run_and_compare_all(w, steps=1)
     for split in (64, 2048):
         _run_and_compare_all(w.replace(name=f"ragged_mixed_s{split}"), split_tokens=split)
-    # 257 block slots per unit: scores from the separate scoring kernel instead of the
-    # selection kernel's own.
-    _run_and_compare_all(w.replace(name="ragged_mixed_two_kernel", t_cap=257 * 16), steps=1)
+    # 257 block slots per unit: the 512-thread selection that forms its own scores; 513:
+    # scores from the separate scoring kernel.
+    for n_cap in (257, 513):
+        _run_and_compare_all(w.replace(name=f"ragged_mixed_{n_cap}", t_cap=n_cap * 16), steps=1)
 
 
 @pytest.mark.parametrize("G,d,dtype", [(1, 128, "bf16"), (3, 128, "bf16"), (8, 128, "bf16"),
@@ -378,11 +379,12 @@ def test_selection_delta_random_lists():
         assert list(bufs.removed[u, :bufs.removed_cnt[u]].cpu()) == list(rr)
 
 
-@pytest.mark.parametrize("t_cap_blocks", [64, 320])
+@pytest.mark.parametrize("t_cap_blocks", [64, 320, 520])
 def test_bad_device_data_is_flagged_not_faulting(t_cap_blocks):
     """seq_len beyond t_cap and out-of-range selection entries are clamped / skipped by the
-    kernels' own checks and reported in the error word (64 block slots: the selection
-    forms its own scores; 320: the separate scoring kernel)."""
+    kernels' own checks and reported in the error word (64 and 320 block slots: the
+    selection forms its own scores, with 256 and 512 threads; 520: the separate scoring
+    kernel)."""
     w = small_workload("tiny")
     w = w.replace(t_cap=t_cap_blocks * w.policies[0].block)
     inp = generate(w, DEV)

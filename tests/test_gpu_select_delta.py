@@ -105,12 +105,15 @@ def test_select_delta_flags_a_bad_previous_selection():
                            B.removed_cnt, B.workspace)
 
 
-def test_one_kernel_and_two_kernel_selection_agree():
-    """Units of at most 256 block slots (key-side summaries) take the selection kernel that
-    forms the scores itself; one more block slot takes the scoring kernel followed by the
-    selection kernel.  The same cache, queries and eviction logits through both plans give
-    the same scores, selections, eviction masks and differences, bit for bit."""
-    g, n_small = 16, 256
+@pytest.mark.parametrize("n_small", [256, 512])
+def test_one_kernel_and_two_kernel_selection_agree(n_small):
+    """Units of at most 512 block slots (key-side summaries) take the selection kernel that
+    forms the scores itself, with 256 threads up to 256 slots and 512 threads above; 513
+    slots take the scoring kernel followed by the selection kernel.  Plans of n_small and
+    n_small + 1 block slots (256 / 257: the two fused widths; 512 / 513: fused and two
+    kernels) on the same cache, queries and eviction logits give the same scores,
+    selections, eviction masks and differences, bit for bit."""
+    g = 16
     pols = (HeadPolicy(MODE_RETRIEVAL, block=g, sub_block=g, top_k=12, force_sink=1, force_last=1),
             HeadPolicy(MODE_NOSA, block=g, sub_block=g, top_k=8, k_evict=24),
             HeadPolicy(MODE_STREAMING, block=g, sub_block=g, sink_tokens=16, local_tokens=64),
