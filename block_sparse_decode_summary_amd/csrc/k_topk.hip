@@ -41,8 +41,8 @@
 // Plans whose units have at most 512 block slots and key-side summaries of at most 256
 // bytes per row skip the separate scoring kernel: k_select_fused forms each unit's scores
 // in its own selection workgroup (wave w scores blocks 64w .. 64w+63, each lane one
-// block, into the register the selection reads), with the float64 chain of k_score, so
-// the scores are the same bits.  Larger units keep k_score: one CU streams a unit's
+// block, into the register the selection reads), with the float64 chain of k_score_sum,
+// so the scores are the same bits.  Larger units keep k_score_sum: one CU streams a unit's
 // summaries far more slowly than the whole GPU scoring its tiles in parallel.
 #include <climits>
 #include <type_traits>
