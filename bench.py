@@ -114,51 +114,160 @@ def measured_traffic(workload: str):
         return None
 
 
-def cpu_baseline(w, inp, seconds: float, seed: int = 0, ed: bool = False):
-    """Time the oracle on a bounded sample of this workload's units, one step each."""
+# ---- CPU baseline: the oracle on the host's cores ----------------------------------------
+#
+# A pool of worker processes, started before this process touches the GPU (spawned
+# interpreters that import only NumPy and the oracle, one BLAS thread each).  After the GPU
+# timing, each worker receives its share of a seeded sample of the workload's units (the
+# same tensors the GPU read), widens them to float64 and builds their summaries (untimed,
+# as the GPU's are resident), then runs the oracle's decode step over them a given number
+# of times; the wall time runs from the "run" message to the last worker's answer.
+
+def _oracle_worker(conn) -> None:
+    import time as _time
+
     import numpy as np
     from threadpoolctl import threadpool_limits
 
     from oracle.delta import selection_delta
     from oracle.pooling import block_summaries, sub_block_means
     from oracle.step import unit_step
-    from workloads import unit_arrays
+
+    def widen(a, dtype):
+        if dtype == "bf16":
+            return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+        return a.astype(np.float64)
+
+    held = []
+    with threadpool_limits(limits=1):
+        while True:
+            msg = conn.recv()
+            if msg[0] == "load":
+                for sp in msg[1]:
+                    K, V = widen(sp["K"], sp["dtype"]), widen(sp["V"], sp["dtype"])
+                    pool_fn = block_summaries if sp["pooling"] == 0 else sub_block_means
+                    summ = pool_fn(K, sp["pol"].block, sp["pol"].sub_block, sp["dtype"])
+                    held.append((sp, K, V, summ, pool_fn))
+                conn.send(("loaded", len(held)))
+            elif msg[0] == "run":
+                reps, done, nbytes = msg[1], 0, 0
+                t0 = _time.perf_counter()
+                for _ in range(reps):
+                    for sp, K, V, summ, pool_fn in held:
+                        pol, T, g = sp["pol"], sp["T"], sp["pol"].block
+                        n_full = T // g
+                        if n_full >= 1:
+                            pool_fn(K[(n_full - 1) * g:n_full * g], g, pol.sub_block, sp["dtype"])
+                        r = unit_step(pol, T, sp["dtype"], sp["q"], K, V, sp["scale"],
+                                      logits=sp["logits"], summaries=summ, ed=sp["ed"],
+                                      pooling=sp["pooling"])
+                        selection_delta(np.zeros(0, np.int64), r.sel)
+                        N = int(np.minimum(g, T - r.sel * g).clip(min=0).sum())
+                        nbytes += 2 * sp["d"] * sp["e"] * N + sp["fixed_bytes"]
+                        done += 1
+                conn.send(("done", _time.perf_counter() - t0, nbytes, done))
+            else:
+                conn.close()
+                return
+
+
+class OraclePool:
+    """Worker processes for the CPU baseline (start before the GPU is touched)."""
+
+    def __init__(self, n: int):
+        import multiprocessing as mp
+        ctx = mp.get_context("spawn")
+        saved = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS",
+                                                "MKL_NUM_THREADS")}
+        os.environ.update({k: "1" for k in saved})
+        self.conns, self.procs = [], []
+        try:
+            for _ in range(n):
+                a, b = ctx.Pipe()
+                p = ctx.Process(target=_oracle_worker, args=(b,), daemon=True)
+                p.start()
+                self.conns.append(a)
+                self.procs.append(p)
+        finally:
+            for k, v in saved.items():
+                if v is None:
+                    os.environ.pop(k, None)
+                else:
+                    os.environ[k] = v
+
+    def close(self) -> None:
+        for c in self.conns:
+            try:
+                c.send(("stop",))
+            except Exception:
+                pass
+        for p in self.procs:
+            p.join(timeout=10)
+            if p.is_alive():
+                p.terminate()
+
+
+def cpu_baseline(pool: OraclePool, w, inp, seconds: float, seed: int = 0, ed: bool = False,
+                 max_units: int = 128):
+    """Time the oracle on a bounded sample of this workload's units on the pool's cores."""
+    import numpy as np
+    import torch
+
     from workloads.generate import unit_logits
 
+    n = len(pool.conns)
+    rng = np.random.default_rng(seed)
+    units = sorted(rng.permutation(w.num_units)[:max_units].tolist())
     scale = 1.0 / math.sqrt(w.head_dim)
-    order = np.random.default_rng(seed).permutation(w.num_units)
     e, d, G = w.elem_bytes, w.head_dim, w.group
-    done, spent, nbytes = 0, 0.0, 0
-    with threadpool_limits(limits=1):
-        for u in order:
-            b, h = divmod(int(u), w.num_kv_heads)
-            p = w.policies[u]
-            T, g = w.seq_lens[b], p.block
-            q_rows, K, V = unit_arrays(inp, b, h)
-            logits = unit_logits(inp, int(u))
-            pool_fn = block_summaries if w.pooling == 0 else sub_block_means
-            summ = pool_fn(K, p.block, p.sub_block, w.dtype)   # resident, not timed
-            n_full = T // g
-            t0 = time.perf_counter()
-            if n_full >= 1:
-                pool_fn(K[(n_full - 1) * g:n_full * g], g, p.sub_block, w.dtype)
-            r = unit_step(p, T, w.dtype, q_rows, K, V, scale, logits=logits, summaries=summ, ed=ed,
-                          pooling=w.pooling)
-            selection_delta(np.zeros(0, np.int64), r.sel)
-            spent += time.perf_counter() - t0
-            N = int(np.minimum(g, T - r.sel * g).clip(min=0).sum())
-            rr = w.summary_rows_per_block(int(u))
-            nbytes += 2 * d * e * N + (n_full * rr * d * e if p.mode != 1 else 0) \
-                + (g * d * e + rr * d * e if n_full else 0) + 3 * G * d * e + G * 4
-            done += 1
-            if spent >= seconds:
-                break
+    raw = torch.int16 if w.dtype == "bf16" else torch.float32
+    shares = [[] for _ in range(n)]
+    load = [0] * n
+    # Longest first, each to the least loaded worker (a unit's cost grows with its length).
+    units.sort(key=lambda u: -w.seq_lens[u // w.num_kv_heads])
+    for u in units:
+        i = load.index(min(load))
+        b, h = divmod(int(u), w.num_kv_heads)
+        load[i] += w.seq_lens[b] + 1
+        p = w.policies[u]
+        T, g = w.seq_lens[b], p.block
+        n_full = T // g
+        rr = w.summary_rows_per_block(int(u))
+        host = lambda x: x.to("cpu").view(raw).numpy()
+        shares[i].append(dict(
+            pol=p, T=T, dtype=w.dtype, pooling=w.pooling, ed=ed, scale=scale, d=d, e=e,
+            q=inp.q[b, h * G:(h + 1) * G].to("cpu").to(torch.float64).numpy(),
+            K=host(inp.K[b, h, :T]).view(np.uint16) if w.dtype == "bf16" else host(inp.K[b, h, :T]),
+            V=host(inp.V[b, h, :T]).view(np.uint16) if w.dtype == "bf16" else host(inp.V[b, h, :T]),
+            logits=unit_logits(inp, int(u)),
+            fixed_bytes=(n_full * rr * d * e if p.mode != 1 else 0)
+            + (g * d * e + rr * d * e if n_full else 0) + 3 * G * d * e + G * 4))
+    for c, sh in zip(pool.conns, shares):
+        c.send(("load", sh))
+    for c in pool.conns:
+        assert c.recv()[0] == "loaded"
+    # One pass to size the repetitions to about `seconds` of CPU work in total.
+    t0 = time.perf_counter()
+    for c in pool.conns:
+        c.send(("run", 1))
+    cpu_one = sum(c.recv()[1] for c in pool.conns)
+    reps = max(1, int(round(seconds / max(cpu_one, 1e-6))))
+    t0 = time.perf_counter()
+    for c in pool.conns:
+        c.send(("run", reps))
+    res = [c.recv() for c in pool.conns]
+    wall = time.perf_counter() - t0
+    nbytes = sum(r[2] for r in res)
+    steps = sum(r[3] for r in res)
+    cpu = sum(r[1] for r in res)
     return {
-        "value": nbytes / spent / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-        "sample": f"{done} of {w.num_units} (sequence, kv head) units of {w.name}, one step each "
-                  f"(newest-block summary + scores + selection + attention + delta; the other "
-                  f"summaries precomputed as on the GPU), float64 NumPy, 1 thread; "
-                  f"{nbytes / 1e6:.1f} MB algorithmic in {spent:.2f} s",
+        "value": nbytes / wall / 1e9, "unit": "GB/s", "cores": n, "kind": "oracle",
+        "sample": f"{len(units)} of {w.num_units} (sequence, kv head) units of {w.name} (seeded "
+                  f"sample), each run {reps} times ({steps} unit-steps: newest-block summary + "
+                  f"scores + selection + attention + delta; the other summaries precomputed as "
+                  f"on the GPU), float64 NumPy oracle in {n} worker processes with 1 BLAS "
+                  f"thread each; {nbytes / 1e6:.1f} MB algorithmic in {wall:.2f} s wall "
+                  f"({cpu:.1f} s of CPU time)",
     }
 
 
@@ -186,7 +295,10 @@ def main() -> int:
                          "set (fx_compact_update), timed as its own phase")
     ap.add_argument("--separate-delta", action="store_true",
                     help="fx_select then fx_selection_delta instead of fx_select_delta")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="CPU time (summed over the workers) the oracle baseline runs for")
+    ap.add_argument("--cpu-workers", type=int, default=16,
+                    help="most oracle worker processes (the pool takes min(this, usable cores))")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-reference", action="store_true",
                     help="after timing, run one plain 1 GiB device copy (scales HBM counters)")
@@ -198,6 +310,18 @@ def main() -> int:
               file=sys.stderr)
         return 2
 
+    # The oracle's worker processes start before this process touches the GPU.
+    pool = None
+    if not args.no_cpu_baseline:
+        pool = OraclePool(min(len(os.sched_getaffinity(0)), args.cpu_workers))
+    try:
+        return run(args, pool)
+    finally:
+        if pool is not None:
+            pool.close()
+
+
+def run(args, pool) -> int:
     import numpy as np
     import torch
 
@@ -313,7 +437,8 @@ def main() -> int:
     timed = range(args.warmup, n_ev)
     moved_main = hist_moved.clone() if args.compact else None   # the later loops overwrite it
     step_ms = [ev_s0[i].elapsed_time(ev_s1[i]) for i in timed]
-    ms_per_step = float(np.mean(step_ms))
+    ms_per_step = float(np.median(step_ms))
+    ms_per_step_mean = float(np.mean(step_ms))
 
     def marked_loop(marks, separate=False):
         """The timed steps again (no token appends), with events at the given marks;
@@ -430,7 +555,7 @@ def main() -> int:
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] timing the CPU oracle on a sample (~{args.cpu_seconds:.0f} s)")
-        cpu = cpu_baseline(w, inp, args.cpu_seconds, ed=args.ed)
+        cpu = cpu_baseline(pool, w, inp, args.cpu_seconds, ed=args.ed)
         log(f"[bench] oracle: {cpu['value']:.4f} GB/s ({cpu['sample']})")
 
     shapes = {
@@ -446,6 +571,7 @@ def main() -> int:
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step_mean": round(ms_per_step_mean, 5),
         "us_per_step": round(ms_per_step * 1e3, 2),
         "step_us_p10_p50_p90": [round(float(np.percentile(step_ms, p)) * 1e3, 2) for p in (10, 50, 90)],
         "frac_of_hbm_peak": round(value / HBM_PEAK_GBS, 4),

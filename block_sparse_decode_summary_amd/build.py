@@ -2,8 +2,9 @@
 
     python -m block_sparse_decode_summary_amd.build
 
-Compiles every csrc/*.hip with hipcc into objects under _build/ (next to this
-package) and links block_sparse_decode_summary_amd/libfx.so.  Always rebuilds.
+Compiles every csrc/*.hip with hipcc for gfx950 and every csrc/*.cpp (host code, no HIP
+header) with the host C++ compiler into objects under _build/ (next to this package) and
+links block_sparse_decode_summary_amd/libfx.so.  Always rebuilds.
 """
 from __future__ import annotations
 
@@ -32,13 +33,21 @@ CFLAGS = [
 ]
 
 
+CXX = os.environ.get("CXX", "g++")
+CXXFLAGS = ["-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", f"-I{INCLUDE}", f"-I{CSRC}"]
+
+
 def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
+                  if f.endswith(".hip") or f.endswith(".cpp"))
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    if src.endswith(".cpp"):
+        cmd = [CXX, *CXXFLAGS, "-c", src, "-o", obj]
+    else:
+        cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

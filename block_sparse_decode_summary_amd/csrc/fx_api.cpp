@@ -1,15 +1,18 @@
 // libfx host side: plan creation, argument validation, workspace layout, entry points.
 //
-// Everything here runs on the host.  Validation happens before any HIP call, so the
-// error paths work (and are tested) on machines without a GPU.  No C++ exception
-// leaves this file: every entry point catches and maps to a status.
+// Everything here runs on the host and is plain C++ (no HIP header): the device calls
+// go through the fx::dev_* functions and the kernel launchers of the .hip files.
+// Validation happens before any device call, so the error paths work (and are tested,
+// with stand-ins for those functions and under the address and undefined-behaviour
+// sanitizers) on machines without a GPU.  No C++ exception leaves this file: every
+// entry point catches and maps to a status.
 #include <algorithm>
 #include <climits>
 #include <cmath>
 #include <cstring>
 #include <new>
 
-#include "fx_internal.h"
+#include "fx_plan.h"
 
 namespace {
 
@@ -89,6 +92,41 @@ int64_t max_selected(const fx_head_policy& p, int64_t n_cap) {
       m = (int64_t)p.top_k + p.k_evict + 2;
   }
   return std::min(m, n_cap);
+}
+
+}  // namespace
+
+namespace fx {
+
+// The selection keeps keys, candidate flags and old eviction words in registers when
+// every unit has at most kTopkRegBlocks block slots; larger units use the workspace.
+bool topk_in_registers(const fx_plan* p) { return p->max_n_cap <= kTopkRegBlocks; }
+
+// Scores and selection in one kernel: key-side summaries, summary rows of at most 256
+// bytes (a wave's 64-row tile then fits in 64 registers per lane) and at most
+// kFusedSelectBlocks block slots per unit (one 64-block tile per wave, 256 threads per
+// unit up to 256 block slots, else 512).  Larger units keep the separate scoring kernel:
+// one CU cannot stream a large unit's summaries as fast as the whole GPU scoring it tile
+// by tile.
+bool select_fused(const fx_plan* p) {
+  const int row_bytes = p->desc.head_dim * (p->desc.dtype == FX_BF16 ? 2 : 4);
+  return p->any_scored && p->desc.pooling == FX_POOL_KEY && row_bytes <= 256 &&
+         p->max_n_cap <= kFusedSelectBlocks;
+}
+
+}  // namespace fx
+
+namespace {
+
+// Decode partials for `grid` segments: a head and a tail piece per segment.
+fx::DecodeScratch decode_scratch_layout(int64_t grid, int G, int d) {
+  fx::DecodeScratch s;
+  const size_t slots = (size_t)grid * 2;
+  s.part_o = 0;
+  s.part_ml = align_up(slots * G * d * 4, 256);
+  s.seg = s.part_ml + align_up(slots * G * 8, 256);
+  s.end = s.seg + align_up((size_t)grid * 8, 256);
+  return s;
 }
 
 fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_plan_t* out) {
@@ -191,13 +229,9 @@ fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_pl
   off += align_up(topk_regs ? 0 : (size_t)p->total_blocks * 4, 256);
   p->ws_bits_off = off;
   off += align_up(topk_regs ? 0 : (size_t)p->mask_words * 3 * 4, 256);
-  const size_t slots = (size_t)p->decode_grid * 2;   // head and tail piece per segment
-  p->ws_part_o_off = off;
-  off += align_up(slots * p->G * d * 4, 256);
-  p->ws_part_ml_off = off;
-  off += align_up(slots * p->G * 8, 256);
-  p->ws_seg_off = off;
-  off += align_up((size_t)p->decode_grid * 8, 256);
+  p->ws_decode = decode_scratch_layout(p->decode_grid, p->G, d);
+  p->ws_decode_off = off;
+  off += p->ws_decode.end;
   p->ws_moves_off = off;
   off += align_up((size_t)units * p->max_sel * 8, 256);
   p->ws_move_cnt_off = off;
@@ -212,8 +246,7 @@ fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_pl
   std::vector<int32_t> host_order(p->host_scored);
   for (int32_t u = 0; u < units; ++u)
     if (p->host_units[u].mode == FX_STREAMING) host_order.push_back(u);
-  if (hipGetDevice(&p->device) != hipSuccess ||
-      hipMalloc(&p->d_table, tab_bytes) != hipSuccess) {
+  if (fx::dev_current(&p->device) != 0 || fx::dev_alloc(&p->d_table, tab_bytes) != 0) {
     delete p;
     return FX_E_HIP;
   }
@@ -222,15 +255,12 @@ fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_pl
   p->d_error = reinterpret_cast<uint32_t*>(base + tab_units);
   p->d_scored = reinterpret_cast<int32_t*>(base + tab_units + 256);
   p->d_order = reinterpret_cast<int32_t*>(base + tab_units + 256 + tab_scored);
-  if (hipMemcpy(p->d_units, p->host_units.data(), sizeof(UnitInfo) * units,
-                hipMemcpyHostToDevice) != hipSuccess ||
-      hipMemcpy(p->d_order, host_order.data(), sizeof(int32_t) * units,
-                hipMemcpyHostToDevice) != hipSuccess ||
+  if (fx::dev_upload(p->d_units, p->host_units.data(), sizeof(UnitInfo) * units) != 0 ||
+      fx::dev_upload(p->d_order, host_order.data(), sizeof(int32_t) * units) != 0 ||
       (p->n_scored > 0 &&
-       hipMemcpy(p->d_scored, p->host_scored.data(), sizeof(int32_t) * p->n_scored,
-                 hipMemcpyHostToDevice) != hipSuccess) ||
-      hipMemset(base + tab_units, 0, 256) != hipSuccess) {
-    (void)hipFree(p->d_table);
+       fx::dev_upload(p->d_scored, p->host_scored.data(), sizeof(int32_t) * p->n_scored) != 0) ||
+      fx::dev_zero(base + tab_units, 256) != 0) {
+    (void)fx::dev_free(p->d_table);
     delete p;
     return FX_E_HIP;
   }
@@ -238,7 +268,7 @@ fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_pl
   return FX_OK;
 }
 
-fx_status hip_status(hipError_t e) { return e == hipSuccess ? FX_OK : FX_E_HIP; }
+fx_status hip_status(int e) { return e == 0 ? FX_OK : FX_E_HIP; }
 
 }  // namespace
 
@@ -256,7 +286,7 @@ fx_status fx_plan_create(const fx_plan_desc* desc, const fx_head_policy* host_po
 fx_status fx_plan_destroy(fx_plan_t plan) {
   if (!plan) return FX_OK;
   fx_status st = FX_OK;
-  if (plan->d_table && hipFree(plan->d_table) != hipSuccess) st = FX_E_HIP;
+  if (plan->d_table && fx::dev_free(plan->d_table) != 0) st = FX_E_HIP;
   delete plan;
   return st;
 }
@@ -304,10 +334,7 @@ const char* fx_status_string(fx_status s) {
 
 fx_status fx_read_error(fx_plan_t p, uint32_t* host_word) {
   if (!p || !host_word) return FX_E_INVALID;
-  if (hipDeviceSynchronize() != hipSuccess) return FX_E_HIP;
-  if (hipMemcpy(host_word, p->d_error, 4, hipMemcpyDeviceToHost) != hipSuccess) return FX_E_HIP;
-  if (hipMemset(p->d_error, 0, 4) != hipSuccess) return FX_E_HIP;
-  return FX_OK;
+  return fx::dev_take_error(p->d_error, host_word) == 0 ? FX_OK : FX_E_HIP;
 }
 
 size_t fx_stream_read_sink_words(size_t bytes) {
@@ -361,8 +388,7 @@ fx_status select_blocks(fx_plan_t p, const void* q, const void* summaries,
                                                 prev_idx, prev_cnt, added, added_cnt, removed,
                                                 removed_cnt, stream));
     if (p->any_scored) {
-      hipError_t e = fx::launch_score(p, q, summaries, seq_lens, scores, stream);
-      if (e != hipSuccess) return FX_E_HIP;
+      if (fx::launch_score(p, q, summaries, seq_lens, scores, stream) != 0) return FX_E_HIP;
     }
     char* ws = static_cast<char*>(workspace);
     return hip_status(fx::launch_topk(p, scores, evict_logits, evicted_mask, seq_lens, sel_idx,
@@ -402,23 +428,29 @@ fx_status fx_select_delta(fx_plan_t p, const void* q, const void* summaries,
 
 namespace {
 
+fx_status check_decode_args(fx_plan_t p, const void* q, const void* K, const void* V,
+                            const int32_t* seq_lens, const int32_t* sel_idx,
+                            const int32_t* sel_cnt, float softmax_scale, const void* out,
+                            const float* lse) {
+  if (!p || !req(q, 16) || !req(K, 16) || !req(V, 16) || !req(seq_lens, 4) ||
+      !req(sel_idx, 4) || !req(sel_cnt, 4) || !req(out, 16) || !opt(lse, 4))
+    return FX_E_INVALID;
+  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return FX_E_INVALID;
+  return FX_OK;
+}
+
 fx_status sparse_decode(fx_plan_t p, const void* q, const void* K, const void* V,
                         const int32_t* seq_lens, const int32_t* sel_idx, const int32_t* sel_cnt,
                         const float* logits, float softmax_scale, void* out, float* lse,
                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (!p || !req(q, 16) || !req(K, 16) || !req(V, 16) || !req(seq_lens, 4) ||
-      !req(sel_idx, 4) || !req(sel_cnt, 4) || !req(out, 16) || !opt(lse, 4) ||
-      !req(workspace, 16))
-    return FX_E_INVALID;
-  if (!(softmax_scale > 0.0f) || !std::isfinite(softmax_scale)) return FX_E_INVALID;
+  fx_status st = check_decode_args(p, q, K, V, seq_lens, sel_idx, sel_cnt, softmax_scale, out, lse);
+  if (st != FX_OK) return st;
+  if (!req(workspace, 16)) return FX_E_INVALID;
   if (workspace_bytes < p->ws_total) return FX_E_WORKSPACE;
   try {
     char* ws = static_cast<char*>(workspace);
     return hip_status(fx::launch_decode(p, q, K, V, seq_lens, sel_idx, sel_cnt, logits,
-                                        softmax_scale, out, lse,
-                                        reinterpret_cast<float*>(ws + p->ws_part_o_off),
-                                        reinterpret_cast<float*>(ws + p->ws_part_ml_off),
-                                        reinterpret_cast<int32_t*>(ws + p->ws_seg_off), stream));
+                                        softmax_scale, out, lse, ws + p->ws_decode_off, stream));
   } catch (...) {
     return FX_E_HIP;
   }
@@ -460,7 +492,7 @@ fx_status fx_compact_update(fx_plan_t p, const void* K, const void* V, const int
     char* ws = static_cast<char*>(workspace);
     return hip_status(fx::launch_compact(p, K, V, seq_lens, sel_idx, sel_cnt, slot_map, work_K,
                                          work_V, moved_cnt,
-                                         reinterpret_cast<int2*>(ws + p->ws_moves_off),
+                                         ws + p->ws_moves_off,
                                          reinterpret_cast<int32_t*>(ws + p->ws_move_cnt_off),
                                          stream));
   } catch (...) {

@@ -5,7 +5,7 @@
 
 #include <cstdint>
 
-#include "fx_internal.h"
+#include "fx_plan.h"
 
 namespace fx {
 
@@ -56,9 +56,11 @@ __device__ __forceinline__ void store_from_f64(float* p, double v) { *p = (float
 __device__ __forceinline__ void store_from_f64(bf16_t* p, double v) { *p = f64_to_bf16_rne(v); }
 
 // Monotone uint32 key of a float32 (larger float -> larger key; -0 and +0 equal;
-// NaN maps to 0, below every number).
+// NaN maps to 0, below every number; +-inf rank as the largest / smallest numbers).
+// Any non-finite value sets *nonfinite.
 __device__ __forceinline__ uint32_t f32_key(float f, bool* nonfinite) {
   if (f != f) { *nonfinite = true; return 0u; }
+  if (__builtin_isinf(f)) *nonfinite = true;
   if (f == 0.0f) f = 0.0f;
   const uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);

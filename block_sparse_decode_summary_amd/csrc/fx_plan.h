@@ -1,8 +1,9 @@
-// Internal declarations shared by the host code and the kernel launchers of libfx.
+// Internal declarations shared by the host code (fx_api.cpp) and the kernel files of
+// libfx.  Host-only: no HIP header is needed to compile this file, so the plan logic,
+// argument validation and workspace layout build with a plain C++ compiler as well
+// (the CPU checks of the host path do that, with stand-ins for the device calls).
 // Not part of the ABI (include/fx.h is).
 #pragma once
-
-#include <hip/hip_runtime.h>
 
 #include <cstddef>
 #include <cstdint>
@@ -24,6 +25,8 @@ constexpr uint64_t kStreamReadSpan = 1ull << 20;   // bytes per workgroup of fx_
 constexpr int kMaxTcap = 1 << 24;
 constexpr int kTopkRegBlocks = 8192;   // selection keeps keys in registers up to this n_cap
 constexpr int kFusedSelectBlocks = 512;   // scores formed inside the selection up to this n_cap
+constexpr int kMaxScoreRows = 64;     // summary rows per block under score-side pooling
+constexpr int kMaxCompactSlots = 2048;   // compaction slots per unit (LDS lists)
 
 // Per-unit policy as the kernels read it (device table owned by the plan).
 struct UnitInfo {
@@ -49,8 +52,13 @@ struct UnitInfo {
 };
 static_assert(sizeof(UnitInfo) == 88, "UnitInfo layout");
 
-constexpr int kMaxScoreRows = 64;     // summary rows per block under score-side pooling
-constexpr int kMaxCompactSlots = 2048;   // compaction slots per unit (LDS lists)
+// Byte offsets of the decode partials inside a scratch buffer (the caller's workspace).
+struct DecodeScratch {
+  size_t part_o = 0;     // float [decode_grid][2][G][d]   (head, tail pieces)
+  size_t part_ml = 0;    // float2 [decode_grid][2][G]     (m, l)
+  size_t seg = 0;        // int2 [decode_grid]             (unit, pieces)
+  size_t end = 0;        // first byte past the three arrays
+};
 
 }  // namespace fx
 
@@ -90,9 +98,8 @@ struct fx_plan {
   size_t ws_scores_off = 0;      // float [total_blocks]
   size_t ws_keys_off = 0;        // uint32 [total_blocks]     (top-k keys, workspace path only)
   size_t ws_bits_off = 0;        // uint32 [3 * mask_words]   (top-k bitmaps, workspace path only)
-  size_t ws_part_o_off = 0;      // float [decode_grid][2][G][d]   (head, tail pieces)
-  size_t ws_part_ml_off = 0;     // float2 [decode_grid][2][G]     (m, l)
-  size_t ws_seg_off = 0;         // int2 [decode_grid]             (unit, pieces)
+  fx::DecodeScratch ws_decode;   // decode partials, from ws_decode_off
+  size_t ws_decode_off = 0;
   size_t ws_moves_off = 0;       // int2 [units][max_sel]          (compaction moves)
   size_t ws_move_cnt_off = 0;    // int32 [units]
   size_t ws_total = 0;
@@ -100,47 +107,59 @@ struct fx_plan {
 
 namespace fx {
 
-// Kernel launchers (one per .hip file).  They assume validated arguments.
-hipError_t launch_build_summaries(const fx_plan* p, const void* K, const int32_t* seq_lens,
-                                  int32_t block_begin, int32_t block_end, void* summaries,
-                                  hipStream_t stream);
-hipError_t launch_score(const fx_plan* p, const void* q, const void* summaries,
-                        const int32_t* seq_lens, float* scores, hipStream_t stream);
+// Kernel launchers (one per .hip file).  They assume validated arguments and return 0 or
+// the HIP error code of the failed launch.
+int launch_build_summaries(const fx_plan* p, const void* K, const int32_t* seq_lens,
+                           int32_t block_begin, int32_t block_end, void* summaries,
+                           hipStream_t stream);
+int launch_score(const fx_plan* p, const void* q, const void* summaries, const int32_t* seq_lens,
+                 float* scores, hipStream_t stream);
 // prev_idx == nullptr: no delta; else also the differences against prev (fused into
 // the register path, a second kernel on the workspace path).
-hipError_t launch_topk(const fx_plan* p, const float* scores, const float* logits,
-                       uint32_t* mask, const int32_t* seq_lens, int32_t* sel_idx,
-                       int32_t* sel_cnt, uint32_t* ws_keys, uint32_t* ws_bits,
-                       const int32_t* prev_idx, const int32_t* prev_cnt, int32_t* added,
-                       int32_t* added_cnt, int32_t* removed, int32_t* removed_cnt,
-                       hipStream_t stream);
+int launch_topk(const fx_plan* p, const float* scores, const float* logits, uint32_t* mask,
+                const int32_t* seq_lens, int32_t* sel_idx, int32_t* sel_cnt, uint32_t* ws_keys,
+                uint32_t* ws_bits, const int32_t* prev_idx, const int32_t* prev_cnt,
+                int32_t* added, int32_t* added_cnt, int32_t* removed, int32_t* removed_cnt,
+                hipStream_t stream);
+int launch_select_fused(const fx_plan* p, const void* q, const void* summaries, float* scores,
+                        const float* logits, uint32_t* mask, const int32_t* seq_lens,
+                        int32_t* sel_idx, int32_t* sel_cnt, const int32_t* prev_idx,
+                        const int32_t* prev_cnt, int32_t* added, int32_t* added_cnt,
+                        int32_t* removed, int32_t* removed_cnt, hipStream_t stream);
+// logits == nullptr: plain attention; else each NOSA unit's token of block j also adds
+// logits[block_off + j] to its attention logit.  scratch: the decode partials, laid out
+// as p->ws_decode says.
+int launch_decode(const fx_plan* p, const void* q, const void* K, const void* V,
+                  const int32_t* seq_lens, const int32_t* sel_idx, const int32_t* sel_cnt,
+                  const float* logits, float softmax_scale, void* out, float* lse,
+                  void* scratch, hipStream_t stream);
+int launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
+// moves: int2 [units][max_sel] in the workspace.
+int launch_compact(const fx_plan* p, const void* K, const void* V, const int32_t* seq_lens,
+                   const int32_t* sel_idx, const int32_t* sel_cnt, int32_t* slot_map,
+                   void* work_K, void* work_V, int32_t* moved_cnt, void* moves,
+                   int32_t* move_cnt, hipStream_t stream);
+int launch_delta(const fx_plan* p, const int32_t* prev_idx, const int32_t* prev_cnt,
+                 const int32_t* cur_idx, const int32_t* cur_cnt, int32_t* added,
+                 int32_t* added_cnt, int32_t* removed, int32_t* removed_cnt, hipStream_t stream);
+
 bool topk_in_registers(const fx_plan* p);   // else keys and bitmaps use the workspace
 // Scores formed by the selection kernel itself (no k_score launch, no score reload).
 bool select_fused(const fx_plan* p);
-hipError_t launch_select_fused(const fx_plan* p, const void* q, const void* summaries,
-                               float* scores, const float* logits, uint32_t* mask,
-                               const int32_t* seq_lens, int32_t* sel_idx, int32_t* sel_cnt,
-                               const int32_t* prev_idx, const int32_t* prev_cnt, int32_t* added,
-                               int32_t* added_cnt, int32_t* removed, int32_t* removed_cnt,
-                               hipStream_t stream);
-// logits == nullptr: plain attention; else each NOSA unit's token of block j also adds
-// logits[block_off + j] to its attention logit.
-hipError_t launch_decode(const fx_plan* p, const void* q, const void* K, const void* V,
-                         const int32_t* seq_lens, const int32_t* sel_idx,
-                         const int32_t* sel_cnt, const float* logits, float softmax_scale,
-                         void* out, float* lse, float* part_o, float* part_ml, int32_t* seg_rec,
-                         hipStream_t stream);
+
 // Resident decode workgroups on the current device (0: error); ed: the instantiation
 // with the eviction-logit term.
 int decode_grid(const fx_plan* p, bool ed);
-hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
-hipError_t launch_compact(const fx_plan* p, const void* K, const void* V, const int32_t* seq_lens,
-                          const int32_t* sel_idx, const int32_t* sel_cnt, int32_t* slot_map,
-                          void* work_K, void* work_V, int32_t* moved_cnt, int2* moves,
-                          int32_t* move_cnt, hipStream_t stream);
-hipError_t launch_delta(const fx_plan* p, const int32_t* prev_idx, const int32_t* prev_cnt,
-                        const int32_t* cur_idx, const int32_t* cur_cnt, int32_t* added,
-                        int32_t* added_cnt, int32_t* removed, int32_t* removed_cnt,
-                        hipStream_t stream);
+
+// Device runtime calls the host code makes (HIP in the library).  Each returns 0 or an
+// error code.
+int dev_current(int* device);
+int dev_alloc(void** ptr, size_t bytes);
+int dev_free(void* ptr);
+int dev_upload(void* dst, const void* src, size_t bytes);   // synchronous host -> device
+int dev_zero(void* dst, size_t bytes);                      // synchronous
+// Waits for the current device, copies the error word at dev_word to *host_word and
+// clears it.
+int dev_take_error(uint32_t* dev_word, uint32_t* host_word);
 
 }  // namespace fx

@@ -200,10 +200,11 @@ __global__ __launch_bounds__(NT) void k_compact_copy(
 
 }  // namespace
 
-hipError_t launch_compact(const fx_plan* p, const void* K, const void* V, const int32_t* seq_lens,
-                          const int32_t* sel_idx, const int32_t* sel_cnt, int32_t* slot_map,
-                          void* work_K, void* work_V, int32_t* moved_cnt, int2* moves,
-                          int32_t* move_cnt, hipStream_t stream) {
+int launch_compact(const fx_plan* p, const void* K, const void* V, const int32_t* seq_lens,
+                   const int32_t* sel_idx, const int32_t* sel_cnt, int32_t* slot_map,
+                   void* work_K, void* work_V, int32_t* moved_cnt, void* moves_raw,
+                   int32_t* move_cnt, hipStream_t stream) {
+  int2* moves = static_cast<int2*>(moves_raw);
   k_compact_plan<<<dim3((unsigned)p->units), 64, 0, stream>>>(
       p->d_units, seq_lens, sel_idx, sel_cnt, slot_map, moves, move_cnt, moved_cnt, p->d_error,
       p->desc.num_kv_heads, p->desc.t_cap, p->max_sel);

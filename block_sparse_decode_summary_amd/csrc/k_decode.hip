@@ -615,30 +615,34 @@ __global__ __launch_bounds__(1024) void k_combine(
 constexpr int kU = 4;   // tokens per lane group per step
 
 template <typename E, int D, int G>
-hipError_t launch_t(const fx_plan* p, const void* q, const void* K, const void* V,
-                    const int32_t* seq_lens, const int32_t* sel_idx, const int32_t* sel_cnt,
-                    const float* logits, float softmax_scale, void* out, float* lse,
-                    float* part_o, float* part_ml, int2* seg_rec, hipStream_t stream) {
+int launch_t(const fx_plan* p, const void* q, const void* K, const void* V,
+             const int32_t* seq_lens, const int32_t* sel_idx, const int32_t* sel_cnt,
+             const float* logits, float softmax_scale, void* out, float* lse, void* scratch,
+             hipStream_t stream) {
   const int Hkv = p->desc.num_kv_heads, t_cap = p->desc.t_cap;
   const dim3 grid((unsigned)(logits ? p->decode_grid_ed : p->decode_grid));
+  char* base = static_cast<char*>(scratch);
+  float* part_o = reinterpret_cast<float*>(base + p->ws_decode.part_o);
+  float2* part_ml = reinterpret_cast<float2*>(base + p->ws_decode.part_ml);
+  int2* seg_rec = reinterpret_cast<int2*>(base + p->ws_decode.seg);
   // Every argument but the logits is the same for both instantiations.
   auto args = [&](auto kernel) {
     kernel<<<grid, NT, 0, stream>>>(
         p->d_units, static_cast<const E*>(q), static_cast<const E*>(K),
         static_cast<const E*>(V), seq_lens, sel_idx, sel_cnt, logits, softmax_scale * kLog2e,
-        static_cast<E*>(out), lse, part_o, reinterpret_cast<float2*>(part_ml), seg_rec,
-        p->d_error, Hkv, t_cap, p->max_sel, p->units, p->split);
+        static_cast<E*>(out), lse, part_o, part_ml, seg_rec, p->d_error, Hkv, t_cap, p->max_sel,
+        p->units, p->split);
   };
   if (logits)
     args(k_decode<E, D, G, kU, true>);
   else
     args(k_decode<E, D, G, kU, false>);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  const int e = hipGetLastError();
+  if (e != 0) return e;
   // One thread per output (query row, column).
   constexpr int kCombineThreads = G * D < 1024 ? G * D : 1024;
   k_combine<E, D, G><<<grid, kCombineThreads, 0, stream>>>(
-      seg_rec, static_cast<E*>(out), lse, part_o, reinterpret_cast<const float2*>(part_ml), Hkv);
+      seg_rec, static_cast<E*>(out), lse, part_o, part_ml, Hkv);
   return hipGetLastError();
 }
 
@@ -693,28 +697,28 @@ struct LaunchFn {
   const float* logits;
   float softmax_scale;
   void* out;
-  float *lse, *part_o, *part_ml;
-  int2* seg_rec;
+  float* lse;
+  void* scratch;
   hipStream_t stream;
   template <typename E, int D, int G>
-  hipError_t operator()() const {
+  int operator()() const {
     return launch_t<E, D, G>(p, q, K, V, seq_lens, sel_idx, sel_cnt, logits, softmax_scale, out,
-                             lse, part_o, part_ml, seg_rec, stream);
+                             lse, scratch, stream);
   }
 };
 
 }  // namespace
 
+
 int decode_grid(const fx_plan* p, bool ed) { return with_shape(p, GridFn{ed}); }
 
-hipError_t launch_decode(const fx_plan* p, const void* q, const void* K, const void* V,
-                         const int32_t* seq_lens, const int32_t* sel_idx, const int32_t* sel_cnt,
-                         const float* logits, float softmax_scale, void* out, float* lse,
-                         float* part_o, float* part_ml, int32_t* seg_rec, hipStream_t stream) {
+int launch_decode(const fx_plan* p, const void* q, const void* K, const void* V,
+                  const int32_t* seq_lens, const int32_t* sel_idx, const int32_t* sel_cnt,
+                  const float* logits, float softmax_scale, void* out, float* lse, void* scratch,
+                  hipStream_t stream) {
   if (p->G < 1 || p->G > kMaxGroup) return hipErrorInvalidValue;
   return with_shape(p, LaunchFn{p, q, K, V, seq_lens, sel_idx, sel_cnt, logits, softmax_scale,
-                                out, lse, part_o, part_ml, reinterpret_cast<int2*>(seg_rec),
-                                stream});
+                                out, lse, scratch, stream});
 }
 
 }  // namespace fx

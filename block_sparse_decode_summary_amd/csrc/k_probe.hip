@@ -44,7 +44,7 @@ __global__ __launch_bounds__(kProbeThreads) void k_stream_read(const uint8_t* __
 
 }  // namespace
 
-hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {
+int launch_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {
   const uint64_t span = kStreamReadSpan;
   const uint64_t grid = (bytes + span - 1) / span;
   if (grid == 0) return hipSuccess;

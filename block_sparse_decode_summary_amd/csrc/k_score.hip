@@ -197,7 +197,7 @@ __global__ __launch_bounds__(kWaves * 64) void k_score_sum(
 }
 
 template <typename E, int D>
-hipError_t launch_sum(const fx_plan* p, const void* q, const void* S, const int32_t* seq_lens,
+int launch_sum(const fx_plan* p, const void* q, const void* S, const int32_t* seq_lens,
                       float* scores, hipStream_t stream) {
   const int tiles = (p->max_scored_rows_cap + kTile - 1) / kTile;
   const int quads = (tiles + kWaves - 1) / kWaves;
@@ -210,7 +210,7 @@ hipError_t launch_sum(const fx_plan* p, const void* q, const void* S, const int3
 }
 
 template <typename E, int D, int GM>
-hipError_t launch_gm(const fx_plan* p, const void* q, const void* S, const int32_t* seq_lens,
+int launch_gm(const fx_plan* p, const void* q, const void* S, const int32_t* seq_lens,
                      float* scores, hipStream_t stream) {
   const int tiles = (p->max_scored_rows_cap + kTile - 1) / kTile;
   const int quads = (tiles + kWaves - 1) / kWaves;
@@ -223,7 +223,7 @@ hipError_t launch_gm(const fx_plan* p, const void* q, const void* S, const int32
 }
 
 template <typename E, int D>
-hipError_t launch_t(const fx_plan* p, const void* q, const void* S, const int32_t* seq_lens,
+int launch_t(const fx_plan* p, const void* q, const void* S, const int32_t* seq_lens,
                     float* scores, hipStream_t stream) {
   if (p->desc.pooling != FX_POOL_SCORE_MAX)
     return launch_sum<E, D>(p, q, S, seq_lens, scores, stream);
@@ -241,7 +241,7 @@ hipError_t launch_t(const fx_plan* p, const void* q, const void* S, const int32_
 
 }  // namespace
 
-hipError_t launch_score(const fx_plan* p, const void* q, const void* S, const int32_t* seq_lens,
+int launch_score(const fx_plan* p, const void* q, const void* S, const int32_t* seq_lens,
                         float* scores, hipStream_t stream) {
   const int d = p->desc.head_dim;
   if (p->desc.dtype == FX_BF16)

@@ -109,7 +109,7 @@ __global__ __launch_bounds__(256) void k_build_summaries(
 }
 
 template <typename E, int D>
-hipError_t launch_t(const fx_plan* p, const void* K, const int32_t* seq_lens, int32_t bb,
+int launch_t(const fx_plan* p, const void* K, const int32_t* seq_lens, int32_t bb,
                     int32_t be, void* S, int blocks_per_unit, hipStream_t stream) {
   const dim3 grid((unsigned)((int64_t)blocks_per_unit * p->units));
   k_build_summaries<E, D><<<grid, 256, 0, stream>>>(
@@ -120,7 +120,7 @@ hipError_t launch_t(const fx_plan* p, const void* K, const int32_t* seq_lens, in
 
 }  // namespace
 
-hipError_t launch_build_summaries(const fx_plan* p, const void* K, const int32_t* seq_lens,
+int launch_build_summaries(const fx_plan* p, const void* K, const int32_t* seq_lens,
                                   int32_t bb, int32_t be, void* S, hipStream_t stream) {
   // Upper bound on the blocks any unit can have in [bb, be) once resolved.
   const int64_t n = p->max_n_full_cap;

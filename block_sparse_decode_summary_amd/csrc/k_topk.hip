@@ -29,8 +29,9 @@
 // until at most 64 candidates share it; those are gathered into one wave, which ranks
 // them with lane broadcasts.
 //
-// Mapping: one NT-thread workgroup per unit (NT = 256, or 1024 for plans with few
-// units and more than 1024 block slots).  Thread t owns blocks j = i*NT + t.  When every
+// Mapping: one NT-thread workgroup per unit (NT = 256; 512 for the selection that forms
+// its own scores when units have 257-512 block slots; 1024 for plans with few units and
+// more than 1024 block slots).  Thread t owns blocks j = i*NT + t.  When every
 // unit has at most 8192 block slots the keys, the candidate flags and the old eviction
 // words stay in registers (k_topk_reg), wave ballots of the per-block flags give the
 // bitmap words, and a scan over (row, wave) counts compacts the selection straight into
@@ -77,8 +78,6 @@ constexpr int NT = 1024;
 #undef FX_TOPK_WORKSPACE_PATH
 }  // namespace topk1024
 
-bool topk_in_registers(const fx_plan* p) { return p->max_n_cap <= kTopkRegBlocks; }
-
 namespace {
 
 // Units below which a plan cannot fill the GPU with one 256-thread workgroup each; such
@@ -86,7 +85,7 @@ namespace {
 constexpr int kFewUnits = 128;
 
 template <int NTW, class DA, class LaunchReg>
-hipError_t dispatch_reg(int n, const DA& D, LaunchReg&& launch) {
+int dispatch_reg(int n, const DA& D, LaunchReg&& launch) {
   // n <= kTopkRegBlocks here, so KPT * NTW never exceeds it.
   if (n <= 1 * NTW) launch(std::integral_constant<int, 1>{}, D);
   else if (n <= 2 * NTW) launch(std::integral_constant<int, 2>{}, D);
@@ -100,7 +99,7 @@ hipError_t dispatch_reg(int n, const DA& D, LaunchReg&& launch) {
 
 // Summary element type and head dim of the fused kernel (rows of at most 256 bytes).
 template <class F>
-hipError_t by_element(const fx_plan* p, F&& f) {
+int by_element(const fx_plan* p, F&& f) {
   if (p->desc.dtype == FX_BF16) {
     if (p->desc.head_dim == 128) f(bf16_t{}, std::integral_constant<int, 128>{});
     else f(bf16_t{}, std::integral_constant<int, 64>{});
@@ -112,19 +111,7 @@ hipError_t by_element(const fx_plan* p, F&& f) {
 
 }  // namespace
 
-// Scores and selection in one kernel: key-side summaries, summary rows of at most 256
-// bytes (a wave's 64-row tile then fits in 64 registers per lane) and at most
-// kFusedSelectBlocks block slots per unit: one 64-block tile per wave, 256 threads per
-// unit up to 256 block slots, else 512.  Larger units keep the separate scoring kernel:
-// one CU cannot stream a large unit's summaries as fast as the whole GPU scoring it tile
-// by tile.
-bool select_fused(const fx_plan* p) {
-  const int row_bytes = p->desc.head_dim * (p->desc.dtype == FX_BF16 ? 2 : 4);
-  return p->any_scored && p->desc.pooling == FX_POOL_KEY && row_bytes <= 256 &&
-         p->max_n_cap <= kFusedSelectBlocks;
-}
-
-hipError_t launch_select_fused(const fx_plan* p, const void* q, const void* summaries,
+int launch_select_fused(const fx_plan* p, const void* q, const void* summaries,
                                float* scores, const float* logits, uint32_t* mask,
                                const int32_t* seq_lens, int32_t* sel_idx, int32_t* sel_cnt,
                                const int32_t* prev_idx, const int32_t* prev_cnt, int32_t* added,
@@ -148,7 +135,7 @@ hipError_t launch_select_fused(const fx_plan* p, const void* q, const void* summ
   return hipErrorInvalidValue;   // select_fused() admits no larger units
 }
 
-hipError_t launch_topk(const fx_plan* p, const float* scores, const float* logits, uint32_t* mask,
+int launch_topk(const fx_plan* p, const float* scores, const float* logits, uint32_t* mask,
                        const int32_t* seq_lens, int32_t* sel_idx, int32_t* sel_cnt,
                        uint32_t* ws_keys, uint32_t* ws_bits, const int32_t* prev_idx,
                        const int32_t* prev_cnt, int32_t* added, int32_t* added_cnt,
@@ -158,8 +145,8 @@ hipError_t launch_topk(const fx_plan* p, const float* scores, const float* logit
     topk256::k_topk_mem<<<dim3((unsigned)p->units), topk256::NT, 0, stream>>>(
         p->d_units, scores, logits, mask, seq_lens, sel_idx, sel_cnt, p->d_error, ws_keys, ws_bits,
         p->desc.num_kv_heads, p->desc.t_cap, p->max_sel);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess || !prev_idx) return e;
+    const int e = hipGetLastError();
+    if (e != 0 || !prev_idx) return e;
     // The workspace path leaves the differences to the delta kernel.
     return launch_delta(p, prev_idx, prev_cnt, sel_idx, sel_cnt, added, added_cnt, removed,
                         removed_cnt, stream);

@@ -131,7 +131,8 @@ enum {
   FX_ERR_SEQ_LEN = 1u << 0,        /* a seq_len was outside [0, t_cap]; clamped */
   FX_ERR_SEL_INDEX = 1u << 1,      /* a selection entry was outside [0, n_tot) or not ascending; skipped */
   FX_ERR_SEL_COUNT = 1u << 2,      /* a sel_cnt was outside [0, max_sel]; clamped */
-  FX_ERR_NONFINITE = 1u << 3,      /* a non-finite score or eviction logit; ranked lowest
+  FX_ERR_NONFINITE = 1u << 3,      /* a non-finite score or eviction logit: NaN ranked
+                                      lowest, +-inf ranked as the largest / smallest value
                                       (fx_sparse_decode_ed: counted as 0) */
   FX_ERR_SLOT_MAP = 1u << 4        /* fx_compact_update: a slot row held one block twice and
                                       some selected blocks found no free slot */
@@ -275,9 +276,8 @@ fx_status fx_select(fx_plan_t plan, const void* q, const void* summaries,
 /* fx_select followed by fx_selection_delta(prev, the new selection), in one call: for
  * plans whose units have at most 8192 block slots the differences are formed by the
  * selection kernel itself (no separate kernel).  Arguments as for the two calls; prev_idx /
- * prev_cnt must not be sel_idx / sel_cnt.  prev must be a selection as fx_select writes it
- * for this plan (ascending block indices of the unit): here an entry that is not is
- * skipped and sets FX_ERR_SEL_INDEX (fx_selection_delta takes any lists). */
+ * prev_cnt must not be sel_idx / sel_cnt.  prev is read as fx_selection_delta reads it
+ * (its longest valid prefix; entries past it are ignored and set FX_ERR_SEL_INDEX). */
 fx_status fx_select_delta(fx_plan_t plan, const void* q, const void* summaries,
                           const float* evict_logits, uint32_t* evicted_mask,
                           const int32_t* seq_lens, const int32_t* prev_idx,
@@ -356,9 +356,13 @@ fx_status fx_compact_update(fx_plan_t plan, const void* K, const void* V,
 /* [NOSA-DE] Methodik §2, bullet "Optimierte Speicherlayout" (set differences of
  * block selections drive block swapping); Methodik §1, "Lokalitätsgarantie".
  * Per unit: added = cur \ prev and removed = prev \ cur, each ascending, padded
- * with -1 to max_sel, with their counts.  prev / cur are sel_idx / sel_cnt
- * arrays in fx_select's layout; a prev_cnt of 0 (the first step) makes every
- * current block "added".  |cur| = |prev| - |removed| + |added| holds per unit. */
+ * with -1 to max_sel, with their counts.  prev / cur are sel_idx / sel_cnt arrays in
+ * fx_select's layout; a prev_cnt of 0 (the first step) makes every current block "added".
+ * Each list enters as its longest prefix that is strictly ascending within the unit's
+ * block slots [0, n_cap(u)) (fx_select writes such lists); an entry past that prefix is
+ * ignored and sets FX_ERR_SEL_INDEX, and a count outside [0, max_sel] is clamped and sets
+ * FX_ERR_SEL_COUNT.  |cur| = |prev| - |removed| + |added| holds per unit for the lists
+ * as entered. */
 fx_status fx_selection_delta(fx_plan_t plan, const int32_t* prev_idx, const int32_t* prev_cnt,
                              const int32_t* cur_idx, const int32_t* cur_cnt,
                              int32_t* added, int32_t* added_cnt, int32_t* removed,
