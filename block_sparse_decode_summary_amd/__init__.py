@@ -24,7 +24,8 @@ __all__ = [
     "fx_compact_update", "fx_unit_work_offset", "fx_unit_max_selected", "WorkingSet", "allocate_working_set",
     "FxError", "Plan", "library_path", "load_library",
     "fx_plan_create", "fx_plan_destroy", "fx_build_summaries", "fx_select",
-    "fx_sparse_decode", "fx_sparse_decode_ed", "fx_selection_delta", "fx_select_delta", "fx_read_error", "fx_status_string",
+    "fx_sparse_decode", "fx_sparse_decode_ed", "fx_sparse_decode_noalloc", "fx_noalloc_scratch_bytes",
+    "fx_selection_delta", "fx_select_delta", "fx_read_error", "fx_status_string",
     "fx_stream_read",
     "StepBuffers", "allocate_step_buffers",
 ]
@@ -101,6 +102,9 @@ def load_library(path: Optional[str] = None):
                                     ctypes.c_size_t, _P]),
         "fx_sparse_decode_ed": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
                                        _P, ctypes.c_size_t, _P]),
+        "fx_sparse_decode_noalloc": (_I32, [_P, _P, _P, _P, _P, _P, _P, ctypes.c_float, _P, _P,
+                                            _P]),
+        "fx_noalloc_scratch_bytes": (ctypes.c_size_t, [_P]),
         "fx_selection_delta": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
         "fx_select_delta": (_I32, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
                                    ctypes.c_size_t, _P]),
@@ -318,6 +322,28 @@ def fx_sparse_decode_ed(plan: Plan, q: torch.Tensor, K: torch.Tensor, V: torch.T
         _ptr(lse, "lse", torch.float32, nq, optional=True),
         _ptr(workspace, "workspace", torch.uint8, plan.workspace_bytes), workspace.numel(),
         _stream(stream)))
+
+
+def fx_sparse_decode_noalloc(plan: Plan, q: torch.Tensor, K: torch.Tensor, V: torch.Tensor,
+                             seq_lens: torch.Tensor, sel_idx: torch.Tensor, sel_cnt: torch.Tensor,
+                             softmax_scale: float, out: torch.Tensor, lse: Optional[torch.Tensor],
+                             stream=None) -> None:
+    """fx_sparse_decode without a workspace: the partials live in the library's static
+    per-GPU array, so the call allocates nothing (calls on one GPU must not overlap)."""
+    dt = plan.torch_dtype
+    nq = plan.batch * plan.num_q_heads
+    _check("fx_sparse_decode_noalloc", load_library().fx_sparse_decode_noalloc(
+        plan.handle, _ptr(q, "q", dt, nq * plan.head_dim), _ptr(K, "K", dt, _kv_numel(plan)),
+        _ptr(V, "V", dt, _kv_numel(plan)), _ptr(seq_lens, "seq_lens", torch.int32, plan.batch),
+        _ptr(sel_idx, "sel_idx", torch.int32, plan.units * plan.max_selected),
+        _ptr(sel_cnt, "sel_cnt", torch.int32, plan.units), float(softmax_scale),
+        _ptr(out, "out", dt, nq * plan.head_dim), _ptr(lse, "lse", torch.float32, nq, optional=True),
+        _stream(stream)))
+
+
+def fx_noalloc_scratch_bytes(plan: Plan) -> int:
+    """Bytes of the static array fx_sparse_decode_noalloc uses for this plan."""
+    return int(load_library().fx_noalloc_scratch_bytes(plan.handle))
 
 
 def fx_unit_max_selected(plan: Plan, unit: int) -> int:

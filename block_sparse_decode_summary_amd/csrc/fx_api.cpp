@@ -264,6 +264,11 @@ fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_pl
     delete p;
     return FX_E_HIP;
   }
+  // The no-allocation decode's scratch: the plan device's static array (looked up once
+  // per device, here at set-up, never in the entry point).
+  size_t scratch_bytes = 0;
+  p->static_scratch = fx::dev_static_scratch(&scratch_bytes);
+  p->static_scratch_fits = p->static_scratch != nullptr && p->ws_decode.end <= scratch_bytes;
   *out = p;
   return FX_OK;
 }
@@ -477,6 +482,24 @@ fx_status fx_sparse_decode_ed(fx_plan_t p, const void* q, const void* K, const v
                        p->any_nosa ? evict_logits : nullptr, softmax_scale, out, lse, workspace,
                        workspace_bytes, stream);
 }
+
+fx_status fx_sparse_decode_noalloc(fx_plan_t p, const void* q, const void* K, const void* V,
+                                   const int32_t* seq_lens, const int32_t* sel_idx,
+                                   const int32_t* sel_cnt, float softmax_scale, void* out,
+                                   float* lse, hipStream_t stream) {
+  fx_status st = check_decode_args(p, q, K, V, seq_lens, sel_idx, sel_cnt, softmax_scale, out, lse);
+  if (st != FX_OK) return st;
+  if (!p->static_scratch) return FX_E_HIP;
+  if (!p->static_scratch_fits) return FX_E_WORKSPACE;
+  try {
+    return hip_status(fx::launch_decode(p, q, K, V, seq_lens, sel_idx, sel_cnt, nullptr,
+                                        softmax_scale, out, lse, p->static_scratch, stream));
+  } catch (...) {
+    return FX_E_HIP;
+  }
+}
+
+size_t fx_noalloc_scratch_bytes(fx_plan_t p) { return p ? p->ws_decode.end : 0; }
 
 fx_status fx_compact_update(fx_plan_t p, const void* K, const void* V, const int32_t* seq_lens,
                             const int32_t* sel_idx, const int32_t* sel_cnt, int32_t* slot_map,

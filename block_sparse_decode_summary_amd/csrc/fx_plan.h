@@ -27,6 +27,8 @@ constexpr int kTopkRegBlocks = 8192;   // selection keeps keys in registers up t
 constexpr int kFusedSelectBlocks = 512;   // scores formed inside the selection up to this n_cap
 constexpr int kMaxScoreRows = 64;     // summary rows per block under score-side pooling
 constexpr int kMaxCompactSlots = 2048;   // compaction slots per unit (LDS lists)
+// Decode scratch of fx_sparse_decode_noalloc: one static device array per GPU.
+constexpr size_t kStaticScratchBytes = size_t(8) << 20;
 
 // Per-unit policy as the kernels read it (device table owned by the plan).
 struct UnitInfo {
@@ -52,7 +54,8 @@ struct UnitInfo {
 };
 static_assert(sizeof(UnitInfo) == 88, "UnitInfo layout");
 
-// Byte offsets of the decode partials inside a scratch buffer (the caller's workspace).
+// Byte offsets of the decode partials inside a scratch buffer (the caller's workspace,
+// or the static array of fx_sparse_decode_noalloc).
 struct DecodeScratch {
   size_t part_o = 0;     // float [decode_grid][2][G][d]   (head, tail pieces)
   size_t part_ml = 0;    // float2 [decode_grid][2][G]     (m, l)
@@ -103,6 +106,11 @@ struct fx_plan {
   size_t ws_moves_off = 0;       // int2 [units][max_sel]          (compaction moves)
   size_t ws_move_cnt_off = 0;    // int32 [units]
   size_t ws_total = 0;
+
+  // fx_sparse_decode_noalloc: the plan device's static scratch array (null if that
+  // device's address could not be found) and whether the decode partials fit in it.
+  void* static_scratch = nullptr;
+  bool static_scratch_fits = false;
 };
 
 namespace fx {
@@ -161,5 +169,8 @@ int dev_zero(void* dst, size_t bytes);                      // synchronous
 // Waits for the current device, copies the error word at dev_word to *host_word and
 // clears it.
 int dev_take_error(uint32_t* dev_word, uint32_t* host_word);
+// The static scratch array of the current device (looked up once per device); nullptr
+// when the lookup fails.  *bytes receives its size.
+void* dev_static_scratch(size_t* bytes);
 
 }  // namespace fx

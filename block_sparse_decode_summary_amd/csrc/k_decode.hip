@@ -55,6 +55,7 @@
 // depend on scheduling.  The kernel boundary makes every partial visible to
 // it; no fence is needed inside k_decode (an agent-scope fence per workgroup would
 // write back the L2 each time).
+#include <mutex>
 #include <type_traits>
 
 #include "fx_device.h"
@@ -709,6 +710,11 @@ struct LaunchFn {
 
 }  // namespace
 
+// Decode scratch for the entry point that allocates nothing (fx_sparse_decode_noalloc):
+// one array per GPU in the library's code object, shared by every call on that GPU.
+// Host code never uses the array's name as an address: the device address comes from
+// hipGetSymbolAddress, once per device, at plan creation (dev_static_scratch).
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
 
 int decode_grid(const fx_plan* p, bool ed) { return with_shape(p, GridFn{ed}); }
 
@@ -719,6 +725,22 @@ int launch_decode(const fx_plan* p, const void* q, const void* K, const void* V,
   if (p->G < 1 || p->G > kMaxGroup) return hipErrorInvalidValue;
   return with_shape(p, LaunchFn{p, q, K, V, seq_lens, sel_idx, sel_cnt, logits, softmax_scale,
                                 out, lse, scratch, stream});
+}
+
+void* dev_static_scratch(size_t* bytes) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  *bytes = kStaticScratchBytes;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    addr[dev] = ptr;
+  }
+  return addr[dev];
 }
 
 }  // namespace fx

@@ -325,6 +325,24 @@ fx_status fx_sparse_decode_ed(fx_plan_t plan, const void* q, const void* K, cons
                               float softmax_scale, void* out, float* lse, void* workspace,
                               size_t workspace_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate device memory while decoding: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ * fx_sparse_decode with no workspace argument: its decode partials go to a static device
+ * array of the library, 8 MiB per GPU (one per GPU the library runs on, held until the
+ * process ends; its address is looked up at fx_plan_create, on the plan's device).  The
+ * call allocates nothing.  Arguments, results and errors as for fx_sparse_decode; a plan
+ * whose partials need more than 8 MiB (fx_noalloc_scratch_bytes) is refused with
+ * FX_E_WORKSPACE, and FX_E_HIP means the array's address could not be found.  Every call
+ * on one GPU shares that GPU's array, which keeps the last call's partials (nothing in it
+ * needs clearing): calls whose kernels overlap in time on one GPU race, so they must be
+ * ordered (one stream, or events). */
+fx_status fx_sparse_decode_noalloc(fx_plan_t plan, const void* q, const void* K, const void* V,
+                                   const int32_t* seq_lens, const int32_t* sel_idx,
+                                   const int32_t* sel_cnt, float softmax_scale, void* out,
+                                   float* lse, hipStream_t stream);
+/* Bytes of the static array a plan's fx_sparse_decode_noalloc uses (0 for a NULL plan). */
+size_t fx_noalloc_scratch_bytes(fx_plan_t plan);
+
 /* [NOSA-DE] Methodik §2 (NOSI), bullet "Optimierte Speicherlayout": the cache is held in
  * minimal block units and blocks are swapped by set difference, with no contiguous
  * allocation.  Keeps, per unit, a copy of its selected FULL blocks in a working set of

@@ -11,8 +11,10 @@ namespace stub {
 int alloc_fails = 0;
 int launch_fails = 0;
 int decode_grid = 512;
+bool scratch_missing = false;
 Launch last;
 int launches = 0;
+static unsigned char scratch[fx::kStaticScratchBytes];
 
 static int record(const char* name, const void* a = nullptr, const void* b = nullptr,
                   const void* c = nullptr) {
@@ -49,6 +51,10 @@ int dev_take_error(uint32_t* dev_word, uint32_t* host_word) {
   *host_word = *dev_word;
   *dev_word = 0;
   return 0;
+}
+void* dev_static_scratch(size_t* bytes) {
+  *bytes = sizeof(stub::scratch);
+  return stub::scratch_missing ? nullptr : stub::scratch;
 }
 int decode_grid(const fx_plan*, bool) { return stub::decode_grid; }
 

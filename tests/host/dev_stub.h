@@ -12,6 +12,7 @@ struct Launch {
 extern int alloc_fails;       // dev_alloc fails while nonzero
 extern int launch_fails;      // every launcher returns this code
 extern int decode_grid;       // what fx::decode_grid reports
+extern bool scratch_missing;  // dev_static_scratch finds no array
 extern Launch last;           // the most recent launch
 extern int launches;          // launches so far
 }  // namespace stub

@@ -185,9 +185,12 @@ static void test_layout_and_sizes() {
   const size_t expect = up256(off * 4) + up256(grid * 2 * G * 64 * 4) + up256(grid * 2 * G * 8) +
                         up256(grid * 8) + up256(8 * 32 * 8) + up256(8 * 4);
   CHECK(fx_workspace_bytes(plan) == expect);
+  CHECK(fx_noalloc_scratch_bytes(plan) ==
+        up256(grid * 2 * G * 64 * 4) + up256(grid * 2 * G * 8) + up256(grid * 8));
   CHECK(fx_plan_destroy(plan) == FX_OK);
   CHECK(fx_plan_destroy(nullptr) == FX_OK);
   CHECK(fx_summary_bytes(nullptr) == 0 && fx_max_selected(nullptr) == -1);
+  CHECK(fx_noalloc_scratch_bytes(nullptr) == 0);
 }
 
 static void test_create_failures() {
@@ -328,7 +331,35 @@ static void test_decode() {
   };
   CHECK(ed(nullptr) == FX_E_INVALID);
   CHECK(ed(lg.as<float>()) == FX_OK && stub::last.b == lg.p());
+
+  // The no-allocation decode: partials in the static array, never in a workspace.
+  auto na = [&](void* o) {
+    return fx_sparse_decode_noalloc(plan, q.p(), K.p(), V.p(), lens.as<int32_t>(),
+                                    sel.as<int32_t>(), cnt.as<int32_t>(), 0.125f, o, nullptr,
+                                    nullptr);
+  };
+  size_t sb = 0;
+  void* static_array = fx::dev_static_scratch(&sb);
+  CHECK(na(out.p()) == FX_OK && stub::last.c == static_array);
+  CHECK(na(out.p(4)) == FX_E_INVALID);
   fx_plan_destroy(plan);
+  // Partials larger than the array: refused with FX_E_WORKSPACE.
+  stub::decode_grid = 40000;
+  CHECK(fx_plan_create(&d, pol, &plan) == FX_OK);
+  if (plan) {
+    CHECK(fx_noalloc_scratch_bytes(plan) > fx::kStaticScratchBytes);
+    CHECK(na(out.p()) == FX_E_WORKSPACE);
+    fx_plan_destroy(plan);
+  }
+  stub::decode_grid = 512;
+  // No array address found on the device: FX_E_HIP.
+  stub::scratch_missing = true;
+  CHECK(fx_plan_create(&d, pol, &plan) == FX_OK);
+  if (plan) {
+    CHECK(na(out.p()) == FX_E_HIP);
+    fx_plan_destroy(plan);
+  }
+  stub::scratch_missing = false;
 }
 
 static void test_other_calls() {
