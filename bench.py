@@ -271,6 +271,58 @@ def cpu_baseline(pool: OraclePool, w, inp, seconds: float, seed: int = 0, ed: bo
     }
 
 
+def graph_replay(fx, plan, w, inp, A, Bsel, q, logits, mask, scale, flush_buf, reps):
+    """Median microseconds of one step (newest-block build, fx_select_delta, fx_sparse_decode)
+    and of fx_select + fx_sparse_decode, each captured once in a HIP graph and replayed,
+    with the cache flush (when on) between replays, outside the graph.  Kernel arguments
+    are fixed at capture, so every replay repeats the same step."""
+    import numpy as np
+    import torch
+
+    def capture(fn):
+        fn()                                     # warm-up outside the capture
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g
+
+    def full_step():
+        fx.fx_build_summaries(plan, inp.K, inp.seq_lens, -1, INT32_MAX, A.summaries)
+        fx.fx_select_delta(plan, q, A.summaries, logits, mask, inp.seq_lens, Bsel.sel_idx,
+                           Bsel.sel_cnt, A.sel_idx, A.sel_cnt, A.added, A.added_cnt, A.removed,
+                           A.removed_cnt, A.workspace)
+        fx.fx_sparse_decode(plan, q, inp.K, inp.V, inp.seq_lens, A.sel_idx, A.sel_cnt, scale,
+                            A.out, A.lse, A.workspace)
+
+    def select_decode():
+        fx.fx_select(plan, q, A.summaries, logits, mask, inp.seq_lens, A.sel_idx, A.sel_cnt,
+                     A.workspace)
+        fx.fx_sparse_decode(plan, q, inp.K, inp.V, inp.seq_lens, A.sel_idx, A.sel_cnt, scale,
+                            A.out, A.lse, A.workspace)
+
+    res = {}
+    for key, fn in (("step", full_step), ("select_decode", select_decode)):
+        g = capture(fn)
+        times = []
+        for i in range(reps + 3):
+            if flush_buf is not None:
+                flush_buf.fill_(i & 0xFF)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            if i >= 3:
+                times.append(e0.elapsed_time(e1))
+        res[key + "_us_median"] = round(float(np.median(times)) * 1e3, 2)
+        del g
+    if fx.fx_read_error(plan) != 0:
+        raise SystemExit("device error word set during the graph replays")
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -302,6 +354,9 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-reference", action="store_true",
                     help="after timing, run one plain 1 GiB device copy (scales HBM counters)")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step, and fx_select + fx_sparse_decode, replayed from a "
+                         "captured HIP graph (launches without the host in between)")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -507,6 +562,12 @@ def run(args, pool) -> int:
                  "locality_min": round(float(gamma.min()), 4),
                  "steps_per_query_cycle": len(qs)}
 
+    graph = None
+    if args.graph:
+        graph = graph_replay(fx, plan, w, inp, A, Bsel, qs[0], logits, mask, scale, flush_buf,
+                             args.steps)
+        log(f"[bench] graph replay: {graph}")
+
     if args.copy_reference:
         src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -597,6 +658,8 @@ def run(args, pool) -> int:
     }
     if drift:
         line["selection_drift"] = drift
+    if graph:
+        line["graph_replay"] = graph
     if compact:
         line["compaction"] = compact
     print(json.dumps(line), flush=True)
