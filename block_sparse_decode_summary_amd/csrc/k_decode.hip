@@ -41,13 +41,17 @@
 // out-of-range offset and read zeros without a branch or a memory access.  Loads for
 // the next step of U tokens per lane group are issued before the current step is
 // computed (register double buffering), so two steps are in flight per wave.  Each lane
-// keeps the G query rows' matching 16 bytes in registers, forms G partial dot products
-// (v_dot2_f32_bf16 for bfloat16) and DPP-reduces them across its LPT lanes.  The online
-// softmax runs in base 2 (scores pre-multiplied by scale*log2(e)) per lane group,
-// rescaling o and l only in steps where some running max grew.  For bfloat16 the P.V
-// update takes tokens in pairs: p is rounded to bfloat16 and one v_dot2_f32_bf16 per
-// (row, column) accumulates both tokens.  Lane groups, then waves, merge with the
-// log-sum-exp rule.
+// keeps the G query rows' matching 16 bytes in registers and forms G x U partial dot
+// products (v_dot2_f32_bf16 for bfloat16).  Instead of reducing every one of them across
+// the LPT lanes (and repeating the softmax in all of them), the partials pass through
+// LDS transposed, so that each lane sums the LPT partials of its own (row, token) slots
+// (see Slots): the cross-lane work per step drops from G x U reductions to one LDS round
+// trip, and each score's exponential is taken once.  The online softmax runs in base 2
+// (scores pre-multiplied by scale*log2(e)) per lane group, rescaling o and l only in
+// steps where some running max grew.  For bfloat16 the P.V update takes tokens in pairs:
+// p is rounded to bfloat16, paired within the quad, broadcast along the row (DPP
+// row_newbcast), and one v_dot2_f32_bf16 per (row, column) accumulates both tokens.
+// Lane groups, then waves, merge with the log-sum-exp rule.
 //
 // k_combine (one workgroup per segment, exits unless the segment recorded a unit that
 // continues past it) merges that unit's partials in segment order with the
@@ -82,6 +86,59 @@ struct Lanes<float> {
   static constexpr int EPL = 4;
 };
 
+constexpr int kU = 4;   // tokens per lane group per step (the four lanes of a quad, below)
+
+// Score slots of one step.  A lane group (LPT lanes, one token at a time) forms, for its
+// kU tokens u and G query rows g, LPT partial dot products per (g, u).  They go to LDS
+// and come back transposed: slot k = g * kU + u is summed by the lanes with
+// k = (lane index in the group mod SLOTW) + SLOTW * j, j < SL, so each lane finishes SL
+// scores instead of every lane finishing all G * kU.  With kU = 4 the four lanes of a quad
+// hold one query row's four tokens (their max is two quad permutes) and u = lane & 3.
+// Lanes past the G * kU slots repeat slot k mod G * kU.  Groups of 32 lanes are two rows
+// of 16 that each hold every slot, so row broadcasts reach every lane that needs a value.
+template <typename E, int D, int G>
+struct Slots {
+  static constexpr int LPT = D / Lanes<E>::EPL;
+  static constexpr int NS = G * kU;
+  static constexpr int SLOTW = LPT < 16 ? LPT : 16;
+  static constexpr int SL = (NS + SLOTW - 1) / SLOTW;
+  static constexpr int QPR = SLOTW / kU;   // query rows per slot register
+  // LDS floats per slot and per lane group.  Slot stride LPT + 4 puts the slot bases that
+  // eight lanes read together (one 128-byte LDS cycle of 16-byte reads) on distinct
+  // four-bank groups; a group stride of 16 (LPT 16) or 8 (LPT 8) banks mod 32 keeps the
+  // 32 lanes of one 4-byte write cycle on distinct banks.
+  static constexpr int SS = LPT + 4;
+  static constexpr int kResidue = LPT == 16 ? 16 : LPT == 8 ? 8 : 0;
+  static constexpr int GS = NS * SS + ((kResidue - (NS * SS) % 32) + 32) % 32;
+  static_assert(kU == 4, "a quad holds one query row's tokens");
+};
+
+// Row broadcast of lane `SRC` of this lane's group (row_newbcast: every lane of a row of
+// 16 reads lane SRC of that row).  Groups of 8 take lane SRC or 8 + SRC of the row.
+template <int LPT, int SRC>
+__device__ __forceinline__ float group_bcast(float x) {
+  static_assert(SRC >= 0 && SRC < (LPT < 16 ? LPT : 16), "source lane");
+  const int xi = __float_as_int(x);
+  if constexpr (LPT >= 16) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, xi, 0x150 + SRC, 0xF, 0xF, false));
+  } else {
+    static_assert(LPT == 8, "lane groups of 8, 16 or 32");
+    const int lo = __builtin_amdgcn_update_dpp(0, xi, 0x150 + SRC, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, xi, 0x158 + SRC, 0xF, 0xF, false);
+    return __int_as_float((threadIdx.x & 8) ? hi : lo);
+  }
+}
+
+// Calls f(std::integral_constant<int, I>{}) for I = 0 .. N-1 (indices that must be
+// constants, such as DPP controls).
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 // Partial dot product of this lane's 16 bytes of K with one query row's 16 bytes.
 __device__ __forceinline__ float lane_dot(const uint4& qv, const uint4& kv, bf16_t*) {
   float acc = 0.0f;
@@ -109,14 +166,12 @@ __device__ __forceinline__ void unpack(const uint4& v, float* f, float*) {
 }
 
 // o[g][2w], o[g][2w+1] += p_a * v_a + p_b * v_b for one pair of tokens (a, b) of this
-// lane, with p rounded to bfloat16: v_perm_b32 pairs the two tokens' element of each
-// column into one dword and v_dot2_f32_bf16 does both products and the accumulation.
+// lane, pk[g] holding (p_a, p_b) of query row g as bfloat16: v_perm_b32 pairs the two
+// tokens' element of each column into one dword and v_dot2_f32_bf16 does both products
+// and the accumulation.
 template <int G>
-__device__ __forceinline__ void pv_pair(const float* pa, const float* pb, const uint4& va,
-                                        const uint4& vb, float (*o)[8]) {
-  bf16x2_t pk[G];
-#pragma unroll
-  for (int gg = 0; gg < G; ++gg) pk[gg] = bf16x2_t{(__bf16)pa[gg], (__bf16)pb[gg]};
+__device__ __forceinline__ void pv_pair(const uint32_t* pk, const uint4& va, const uint4& vb,
+                                        float (*o)[8]) {
   const uint32_t a[4] = {va.x, va.y, va.z, va.w};
   const uint32_t b[4] = {vb.x, vb.y, vb.z, vb.w};
 #pragma unroll
@@ -125,8 +180,9 @@ __device__ __forceinline__ void pv_pair(const float* pa, const float* pb, const 
     const bf16x2_t hi = __builtin_bit_cast(bf16x2_t, __builtin_amdgcn_perm(b[w], a[w], 0x07060302u));
 #pragma unroll
     for (int gg = 0; gg < G; ++gg) {
-      o[gg][2 * w] = __builtin_amdgcn_fdot2_f32_bf16(pk[gg], lo, o[gg][2 * w], false);
-      o[gg][2 * w + 1] = __builtin_amdgcn_fdot2_f32_bf16(pk[gg], hi, o[gg][2 * w + 1], false);
+      const bf16x2_t pg = __builtin_bit_cast(bf16x2_t, pk[gg]);
+      o[gg][2 * w] = __builtin_amdgcn_fdot2_f32_bf16(pg, lo, o[gg][2 * w], false);
+      o[gg][2 * w + 1] = __builtin_amdgcn_fdot2_f32_bf16(pg, hi, o[gg][2 * w + 1], false);
     }
   }
 }
@@ -165,9 +221,17 @@ __device__ __forceinline__ UnitTokens unit_tokens(const UnitInfo* units, const i
 
 template <typename E, int D, int G, bool ED>
 struct DecodeLds {
+  using SL = Slots<E, D, G>;
+  // Per wave: its lane groups' partial dot products during the token steps, then, after
+  // the wave's last step of a piece, its (o) of the query rows.  Only the wave itself
+  // writes its area; a barrier separates the merge's reads from the next piece's steps.
+  union WaveArea {
+    float tr[64 / SL::LPT][SL::GS];
+    float o[G][D];
+  };
+  alignas(16) WaveArea wa[NWAVES];
   int blk[kMaxSplit + 1];          // selected block indices of the current token run
   float bias[ED ? kMaxSplit + 1 : 1];   // their eviction logits times log2(e) (ED only)
-  float o[NWAVES][G][D];
   float m[NWAVES][G];
   float l[NWAVES][G];
   int scan[2][NWAVES];
@@ -313,6 +377,18 @@ __global__ __launch_bounds__(NT, 2) void k_decode(
 
   const uint32_t lane_off = (uint32_t)(lane % LPT) * 16u;
   const int lg = lane / LPT, li = lane % LPT;
+  // This lane's score slots (see Slots): where their partial dot products sit in LDS,
+  // and the token u they belong to (the same for every slot of the lane).
+  using SLT = Slots<E, D, G>;
+  constexpr int SL = SLT::SL, QPR = SLT::QPR, SS = SLT::SS, NS = SLT::NS;
+  float* const tr = &L.wa[wave].tr[lg][0];
+  int slot_off[SL];
+#pragma unroll
+  for (int j = 0; j < SL; ++j) {
+    const int k = li % SLT::SLOTW + SLT::SLOTW * j;
+    slot_off[j] = (k < NS ? k : k % NS) * SS;
+  }
+  const int usel = lane & (U - 1);
   constexpr uint32_t kRowBytes = D * sizeof(E);
   bool recorded = false;
   int u = __builtin_amdgcn_readfirstlane(half ? L.first_unit_h : L.first_unit);
@@ -339,14 +415,18 @@ __global__ __launch_bounds__(NT, 2) void k_decode(
     uint4 qv[G];
 #pragma unroll
     for (int gg = 0; gg < G; ++gg) qv[gg] = *reinterpret_cast<const uint4*>(qrow + (size_t)gg * D);
-    float m[G], l[G], o[G][EPL == 8 ? 8 : EPL];
+    // Running max and sum of this lane's slots (a quad shares one query row's max; each
+    // lane sums its own token u), and the output columns of every query row.
+    float m[SL], l[SL], o[G][EPL == 8 ? 8 : EPL];
 #pragma unroll
-    for (int gg = 0; gg < G; ++gg) {
-      m[gg] = kNegBig;
-      l[gg] = 0.0f;
+    for (int j = 0; j < SL; ++j) {
+      m[j] = kNegBig;
+      l[j] = 0.0f;
+    }
+#pragma unroll
+    for (int gg = 0; gg < G; ++gg)
 #pragma unroll
       for (int x = 0; x < EPL; ++x) o[gg][x] = 0.0f;
-    }
     // The unit's rows [0, T) of K and V as buffer resources: rows past T, and masked
     // token slots (sent to kOutOfRange), read as zeros with no memory access.
     const size_t unit_rows = (size_t)u * t_cap;
@@ -389,16 +469,16 @@ __global__ __launch_bounds__(NT, 2) void k_decode(
         int jb[U];
 #pragma unroll
         for (int uu = 0; uu < U; ++uu) {
-          const int i = base + uu * TPW + lg;
-          const int slot = max(0, min((i >> log2g) - p0, np - 1));
+          const int i = base + uu * TPW + lg;   // i >= c0, so the slot is never negative
+          const int slot = min((i >> log2g) - p0, np - 1);
           jb[uu] = L.blk[slot];
           if constexpr (ED) bs[uu] = L.bias[slot];
         }
 #pragma unroll
         for (int uu = 0; uu < U; ++uu) {
           const int i = base + uu * TPW + lg;
-          const int row = jb[uu] * g + (i & (g - 1));
-          ok[uu] = i < w1 && jb[uu] >= 0 && row < T;
+          const int row = (jb[uu] << log2g) | (i & (g - 1));
+          ok[uu] = (i < w1) & (jb[uu] >= 0) & (row < T);   // no short circuit: no branch
           const uint32_t off = ok[uu] ? (uint32_t)row * kRowBytes + lane_off : kOutOfRange;
           kr[uu] = buffer_load16(rk, off);
           vr[uu] = buffer_load16(rv, off);
@@ -406,64 +486,102 @@ __global__ __launch_bounds__(NT, 2) void k_decode(
       };
 
       auto compute_step = [&](const uint4* kr, const uint4* vr, const bool* ok, const float* bs) {
-        float sc[U][G];
+        // Partial dot products to LDS (slot k = g * U + u, the group's LPT lanes side by
+        // side); each lane then sums the LPT partials of its own slots.
 #pragma unroll
-        for (int uu = 0; uu < U; ++uu)
+        for (int gg = 0; gg < G; ++gg)
 #pragma unroll
-          for (int gg = 0; gg < G; ++gg) sc[uu][gg] = lane_dot(qv[gg], kr[uu], (E*)nullptr);
+          for (int uu = 0; uu < U; ++uu)
+            tr[(gg * U + uu) * SS + li] = lane_dot(qv[gg], kr[uu], (E*)nullptr);
+        // Additive term of the lane's token: its block's eviction bias (ED) or -inf when
+        // the token slot is masked.
+        float term[U];
 #pragma unroll
-        for (int uu = 0; uu < U; ++uu)
+        for (int uu = 0; uu < U; ++uu) {
+          float t = 0.0f;
+          if constexpr (ED) t = bs[uu];
+          term[uu] = ok[uu] ? t : -__builtin_inff();
+        }
+        float tsel = term[0];
 #pragma unroll
-          for (int gg = 0; gg < G; ++gg) {
-            float t = group_sum<LPT>(sc[uu][gg]) * scale_log2;
-            if constexpr (ED) t += bs[uu];
-            sc[uu][gg] = ok[uu] ? t : -__builtin_inff();
-          }
-        // Rescale o and l only when some running max of the wave grew (a wave-uniform
-        // branch); otherwise every alpha would be exactly 1.
-        float mx[G];
+        for (int uu = 1; uu < U; ++uu) tsel = usel == uu ? term[uu] : tsel;
+        float sc[SL], mx[SL];
         bool grow = false;
 #pragma unroll
-        for (int gg = 0; gg < G; ++gg) {
-          mx[gg] = m[gg];
+        for (int j = 0; j < SL; ++j) {
+          const float4* src = reinterpret_cast<const float4*>(tr + slot_off[j]);
+          float acc[LPT / 4];
 #pragma unroll
-          for (int uu = 0; uu < U; ++uu) mx[gg] = fmaxf(mx[gg], sc[uu][gg]);
-          grow |= mx[gg] > m[gg];
+          for (int c = 0; c < LPT / 4; ++c) {
+            const float4 v = src[c];
+            acc[c] = (v.x + v.y) + (v.z + v.w);
+          }
+#pragma unroll
+          for (int w = LPT / 8; w >= 1; w >>= 1)
+#pragma unroll
+            for (int c = 0; c < w; ++c) acc[c] += acc[c + w];
+          sc[j] = acc[0] * scale_log2 + tsel;
+          float qm = fmaxf(sc[j], dpp_f<kQuadPerm1032>(sc[j]));
+          qm = fmaxf(qm, dpp_f<kQuadPerm2301>(qm));
+          mx[j] = fmaxf(m[j], qm);
+          grow |= mx[j] > m[j];
         }
+        // Rescale o and l only when some running max of the wave grew (a wave-uniform
+        // branch); otherwise every alpha would be exactly 1.
         if (__builtin_expect(__builtin_amdgcn_ballot_w64(grow) != 0, 0)) {
           // Keep this a branch: if-converting it would run the rescale every step.
           asm volatile("" ::: "memory");
+          float alpha[SL];
 #pragma unroll
-          for (int gg = 0; gg < G; ++gg) {
-            const float alpha = __builtin_amdgcn_exp2f(m[gg] - mx[gg]);
-            m[gg] = mx[gg];
-            l[gg] *= alpha;
-#pragma unroll
-            for (int x = 0; x < EPL; ++x) o[gg][x] *= alpha;
+          for (int j = 0; j < SL; ++j) {
+            alpha[j] = __builtin_amdgcn_exp2f(m[j] - mx[j]);
+            m[j] = mx[j];
+            l[j] *= alpha[j];
           }
+          static_for<0, G>([&](auto gc) {
+            constexpr int gg = decltype(gc)::value;
+            const float al = group_bcast<LPT, (gg % QPR) * U>(alpha[gg / QPR]);
+#pragma unroll
+            for (int x = 0; x < EPL; ++x) o[gg][x] *= al;
+          });
         }
-        float pr[U][G];
+        float p[SL];
 #pragma unroll
-        for (int uu = 0; uu < U; ++uu)
-#pragma unroll
-          for (int gg = 0; gg < G; ++gg) {
-            pr[uu][gg] = __builtin_amdgcn_exp2f(sc[uu][gg] - m[gg]);
-            l[gg] += pr[uu][gg];
-          }
+        for (int j = 0; j < SL; ++j) {
+          p[j] = __builtin_amdgcn_exp2f(sc[j] - m[j]);
+          l[j] += p[j];
+        }
         if constexpr (sizeof(E) == 2) {
           static_assert(U % 2 == 0, "token pairs");
+          // bfloat16 pairs (p_u, p_u+1) of the lane's query row, complete in lanes of even u.
+          uint32_t pk[SL];
 #pragma unroll
-          for (int uu = 0; uu < U; uu += 2) pv_pair<G>(pr[uu], pr[uu + 1], vr[uu], vr[uu + 1], o);
+          for (int j = 0; j < SL; ++j) {
+            const float nb = dpp_f<kQuadPerm1032>(p[j]);
+            pk[j] = __builtin_bit_cast(uint32_t, bf16x2_t{(__bf16)p[j], (__bf16)nb});
+          }
+          static_for<0, U / 2>([&](auto pc) {
+            constexpr int u0 = 2 * decltype(pc)::value;
+            uint32_t pb[G];
+            static_for<0, G>([&](auto gc) {
+              constexpr int gg = decltype(gc)::value;
+              pb[gg] = __float_as_uint(
+                  group_bcast<LPT, (gg % QPR) * U + u0>(__uint_as_float(pk[gg / QPR])));
+            });
+            pv_pair<G>(pb, vr[u0], vr[u0 + 1], o);
+          });
         } else {
-#pragma unroll
-          for (int uu = 0; uu < U; ++uu) {
+          static_for<0, U>([&](auto uc) {
+            constexpr int uu = decltype(uc)::value;
             float vf[EPL];
             unpack(vr[uu], vf, (E*)nullptr);
+            static_for<0, G>([&](auto gc) {
+              constexpr int gg = decltype(gc)::value;
+              const float pb = group_bcast<LPT, (gg % QPR) * U + uu>(p[gg / QPR]);
 #pragma unroll
-            for (int gg = 0; gg < G; ++gg)
-#pragma unroll
-              for (int x = 0; x < EPL; ++x) o[gg][x] = fmaf(pr[uu][gg], vf[x], o[gg][x]);
-          }
+              for (int x = 0; x < EPL; ++x) o[gg][x] = fmaf(pb, vf[x], o[gg][x]);
+            });
+          });
         }
       };
 
@@ -485,33 +603,49 @@ __global__ __launch_bounds__(NT, 2) void k_decode(
       }
     }
 
+    // Every lane of a group takes the group's (m, l) of each query row: m from the row's
+    // quad, l summed over the quad's tokens.
+    float mf[G], lf[G];
+    {
+      float lq[SL];
+#pragma unroll
+      for (int j = 0; j < SL; ++j) {
+        const float t = l[j] + dpp_f<kQuadPerm1032>(l[j]);
+        lq[j] = t + dpp_f<kQuadPerm2301>(t);
+      }
+      static_for<0, G>([&](auto gc) {
+        constexpr int gg = decltype(gc)::value;
+        mf[gg] = group_bcast<LPT, (gg % QPR) * U>(m[gg / QPR]);
+        lf[gg] = group_bcast<LPT, (gg % QPR) * U>(lq[gg / QPR]);
+      });
+    }
     // Merge the lane groups of the wave (partners differ in the lane bits above LPT).
 #pragma unroll
     for (int off = LPT; off < 64; off <<= 1) {
 #pragma unroll
       for (int gg = 0; gg < G; ++gg) {
-        const float m2 = __shfl_xor(m[gg], off);
-        const float l2 = __shfl_xor(l[gg], off);
-        const float M = fmaxf(m[gg], m2);
-        const float x = __builtin_amdgcn_exp2f(m[gg] - M);
+        const float m2 = __shfl_xor(mf[gg], off);
+        const float l2 = __shfl_xor(lf[gg], off);
+        const float M = fmaxf(mf[gg], m2);
+        const float x = __builtin_amdgcn_exp2f(mf[gg] - M);
         const float y = __builtin_amdgcn_exp2f(m2 - M);
-        l[gg] = l[gg] * x + l2 * y;
+        lf[gg] = lf[gg] * x + l2 * y;
 #pragma unroll
         for (int z = 0; z < EPL; ++z) {
           const float o2 = __shfl_xor(o[gg][z], off);
           o[gg][z] = o[gg][z] * x + o2 * y;
         }
-        m[gg] = M;
+        mf[gg] = M;
       }
     }
     if (lg == 0) {
 #pragma unroll
       for (int gg = 0; gg < G; ++gg) {
 #pragma unroll
-        for (int z = 0; z < EPL; ++z) L.o[wave][gg][li * EPL + z] = o[gg][z];
+        for (int z = 0; z < EPL; ++z) L.wa[wave].o[gg][li * EPL + z] = o[gg][z];
         if (li == 0) {
-          L.m[wave][gg] = m[gg];
-          L.l[wave][gg] = l[gg];
+          L.m[wave][gg] = mf[gg];
+          L.l[wave][gg] = lf[gg];
         }
       }
     }
@@ -530,7 +664,7 @@ __global__ __launch_bounds__(NT, 2) void k_decode(
       for (int w = 0; w < NWAVES; ++w) {
         const float x = __builtin_amdgcn_exp2f(L.m[w][gg] - M);
         Ls = fmaf(L.l[w][gg], x, Ls);
-        Os = fmaf(L.o[w][gg][c], x, Os);
+        Os = fmaf(L.wa[w].o[gg][c], x, Os);
       }
       if (whole) {
         const size_t orow = (size_t)b * Hkv * G + (size_t)h * G + gg;
@@ -613,8 +747,6 @@ __global__ __launch_bounds__(1024) void k_combine(
   }
 }
 
-constexpr int kU = 4;   // tokens per lane group per step
-
 template <typename E, int D, int G>
 int launch_t(const fx_plan* p, const void* q, const void* K, const void* V,
              const int32_t* seq_lens, const int32_t* sel_idx, const int32_t* sel_cnt,
@@ -647,6 +779,11 @@ int launch_t(const fx_plan* p, const void* q, const void* K, const void* V,
   return hipGetLastError();
 }
 
+// Resident decode workgroups per CU, at most: small groups fit three, but the mixed
+// serving batch (G = 4) decodes in 141 us with two per CU against 143 us with three, and
+// the NOSA batch in 95 us against 100 us (three cut its equal units into pieces).
+constexpr int kMaxDecodeWgsPerCu = 2;
+
 template <typename E, int D, int G, bool ED>
 int grid_t() {
   int per_cu = 0, cus = 0, dev = 0;
@@ -656,7 +793,7 @@ int grid_t() {
           &per_cu, reinterpret_cast<const void*>(&k_decode<E, D, G, kU, ED>), NT, 0) !=
           hipSuccess)
     return 0;
-  return per_cu * cus;
+  return (per_cu < kMaxDecodeWgsPerCu ? per_cu : kMaxDecodeWgsPerCu) * cus;
 }
 
 // Calls f.template operator()<E, D, G>() for the plan's element type, head dim and group.
