@@ -35,18 +35,17 @@ constexpr int kScoreChunkWords = 32;   // row words staged in LDS at a time
 typedef uint32_t ScoreStage[kScoreTile][kScoreChunkWords + 1];
 
 // qs[c] = ((q_0[c] + q_1[c]) + ...) + q_{G-1}[c] in float64 for the G query rows at
-// qgroup (16-byte aligned, rows D elements apart): each of the first G * D * sizeof(E) / 16
-// threads loads 16 bytes into `rows` (one load each, all in flight together), then the
-// first D threads sum a column each.  Every thread of the workgroup calls this; qs is
-// ready after the caller's next barrier.
+// qgroup (16-byte aligned, rows D elements apart): the threads load the G * D * sizeof(E)
+// / 16 16-byte pieces into `rows` (all in flight together), then sum a column each.
+// Every thread of the workgroup calls this; qs is ready after the caller's next barrier.
 template <typename E, int D>
 __device__ __forceinline__ void group_sum_f64(const E* qgroup, int G, uint4* rows, double* qs) {
   constexpr int QV4 = D * (int)sizeof(E) / 16;
-  const int t = threadIdx.x;
-  if (t < G * QV4) rows[t] = reinterpret_cast<const uint4*>(qgroup)[t];
+  for (int t = threadIdx.x; t < G * QV4; t += blockDim.x)
+    rows[t] = reinterpret_cast<const uint4*>(qgroup)[t];
   __syncthreads();
-  if (t < D) {
-    const E* qe = reinterpret_cast<const E*>(rows);
+  const E* qe = reinterpret_cast<const E*>(rows);
+  for (int t = threadIdx.x; t < D; t += blockDim.x) {
     double a = (double)to_f32(qe[t]);
     for (int g = 1; g < G; ++g) a = a + (double)to_f32(qe[g * D + t]);
     qs[t] = a;
