@@ -154,6 +154,27 @@ def test_ragged_degenerate_lengths_and_mixed_modes():
         _run_and_compare_all(w.replace(name=f"ragged_mixed_{n_cap}", t_cap=n_cap * 16), steps=1)
 
 
+def test_more_units_than_one_scan_chunk():
+    """2080 units (three chunks of the decode's unit scan, which keeps 1024 units in
+    registers), ragged short lengths with empty units, all three modes: every unit against
+    the oracle, with the default segment length and with 64-token segments."""
+    rng = np.random.default_rng(2080)
+    B, Hkv = 520, 4
+    lens = [int(x) for x in rng.integers(0, 200, size=B)]
+    lens[7] = lens[300] = 0
+    pols = []
+    for _ in range(B):
+        pols += [HeadPolicy(MODE_RETRIEVAL, block=16, sub_block=8, top_k=3, force_sink=1, force_last=1),
+                 HeadPolicy(MODE_STREAMING, block=16, sub_block=16, sink_tokens=5, local_tokens=40),
+                 HeadPolicy(MODE_NOSA, block=16, sub_block=8, top_k=2, k_evict=3),
+                 HeadPolicy(MODE_RETRIEVAL, block=16, sub_block=4, budget=float(np.float32(0.3)),
+                            force_sink=1, force_last=1)]
+    w = _custom("many_units", B, 2 * Hkv, Hkv, 64, "bf16", 256, lens, pols)
+    assert w.num_units > 2 * 1024
+    _run_and_compare_all(w)
+    _run_and_compare_all(w.replace(name="many_units_s64"), split_tokens=64)
+
+
 @pytest.mark.parametrize("G,d,dtype", [(1, 128, "bf16"), (3, 128, "bf16"), (8, 128, "bf16"),
                                        (2, 64, "bf16"), (5, 128, "f32"), (8, 64, "f32")])
 def test_group_sizes_and_head_dims(G, d, dtype):
