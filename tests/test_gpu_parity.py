@@ -239,6 +239,34 @@ def test_score_ties_prefer_lower_index():
     assert list(gv.unit(0).sel) == [7, 9, 20]
 
 
+@pytest.mark.parametrize("dtype,t_cap", [("bf16", 12000), ("f32", 12000), ("bf16", 4000)])
+def test_scores_with_wide_range_query_groups(dtype, t_cap):
+    """The query rows of kv head 0 are scaled by 1, 2^-16, 2^16 and 2^-32 within each
+    group: their float64 sums qs need more than 45 significant bits, so the chain's
+    products qs[c] * S[c] are rounded (plain rows nearly always give exact ones), and the scores
+    must still be the oracle's chain bit for bit; kv head 1 keeps plain rows.  t_cap
+    12000 (750 block slots) scores in the tiled scoring kernel, 4000 (250) in the
+    selection kernel that forms its own scores.  Scores, selections and outputs."""
+    Hkv, G, d = 2, 4, 128
+    pols = [HeadPolicy(MODE_RETRIEVAL, block=16, sub_block=4, budget=float(np.float32(0.05)),
+                       force_sink=1, force_last=1),
+            HeadPolicy(MODE_NOSA, block=16, sub_block=8, top_k=24, k_evict=48)]
+    lens = [t_cap, t_cap * 7 // 9]
+    w = _custom(f"wide_q_{dtype}_{t_cap}", 2, G * Hkv, Hkv, d, dtype, t_cap, lens, pols * 2)
+    say(f"[parity] {w.name}")
+    inp = generate(w, DEV)
+    q = inp.q.clone()
+    for g, e in enumerate((0, -16, 16, -32)):
+        q[:, g, :] *= 2.0 ** e        # kv head 0 holds query heads 0..G-1
+    plan = make_plan(w)
+    bufs = fx.allocate_step_buffers(plan, DEV)
+    run_select_decode(plan, bufs, inp, q)
+    gv = GpuView(plan, bufs, w)
+    for u in range(w.num_units):
+        compare_unit(w, u, gv, oracle_unit(inp, u, q))
+    assert fx.fx_read_error(plan) == 0
+
+
 @pytest.mark.parametrize("t_cap", [8192 * 16, 8192 * 16 + 3000])
 def test_many_blocks_per_unit(t_cap):
     """n_cap = 8192 is the largest unit whose selection keys stay in registers; one more
