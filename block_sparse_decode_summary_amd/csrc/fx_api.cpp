@@ -149,8 +149,7 @@ fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_pl
   p->G = desc->num_q_heads / desc->num_kv_heads;
   p->units = units;
   p->host_units.resize(units);
-  int64_t boff = 0, soff = 0, woff = 0, moff = 0, max_sel = 1, max_ncap = 0, max_nfull = 0,
-          work = 0;
+  int64_t boff = 0, soff = 0, woff = 0, moff = 0, max_sel = 1, max_ncap = 0, max_nfull = 0;
   for (int u = 0; u < units; ++u) {
     const fx_head_policy& q = pol[u];
     UnitInfo& ui = p->host_units[u];
@@ -182,8 +181,6 @@ fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_pl
     max_sel = std::max(max_sel, ms);
     max_ncap = std::max(max_ncap, n_cap);
     max_nfull = std::max<int64_t>(max_nfull, desc->t_cap / q.block);
-    const int64_t tok = std::min<int64_t>(ms * q.block, desc->t_cap);
-    work += tok;
     if (q.mode != FX_STREAMING) {
       p->any_scored = true;
       p->host_scored.push_back(u);
@@ -207,8 +204,12 @@ fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_pl
   p->max_n_cap = (int32_t)max_ncap;
   p->max_n_full_cap = (int32_t)max_nfull;
 
-  // Selected tokens of all units, laid end to end, are indexed with 32-bit integers.
-  if (work > INT32_MAX) {
+  // The decode lays the token slots of every unit's selected blocks end to end and indexes
+  // them with 32-bit integers.  A valid list of unit u has at most min(n_cap(u), max_sel)
+  // blocks (max_sel being the lists' row stride), and the decode clamps counts to that.
+  int64_t slots = 0;
+  for (const UnitInfo& ui : p->host_units) slots += std::min<int64_t>(ui.n_cap, max_sel) * ui.g;
+  if (slots > INT32_MAX) {
     delete p;
     return FX_E_UNSUPPORTED;
   }

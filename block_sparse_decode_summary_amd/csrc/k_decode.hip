@@ -12,25 +12,27 @@
 // With exp-delayed eviction scores (the ED instantiation), a NOSA unit's token t of
 // block j has s_t = scale * (q . K_t) + b_j, b_j the block's raw eviction logit: its
 // exponential is formed only inside the softmax.  Other units have no eviction head.
-// The selected tokens of a unit are numbered i = 0 .. N-1 in ascending order; because
-// only the last block of a unit can be partial and selections are ascending, token i
-// lives in selected block i / g at offset i % g.
+// A unit with cnt selected blocks has N = cnt * g token slots, numbered i = 0 .. N-1 in
+// list order: slot i is offset i % g of selected block i / g.  Slots past the sequence
+// end (the tail of a partial last block) and slots of invalid entries are masked: they
+// read zeros without a memory access and take no weight.
 //
-// Work split (stream-K): the units' token ranges, laid end to end in unit order, form
-// one sequence of `total` tokens, cut into equal segments of S = max(ceil(total / P),
+// Work split (stream-K): the units' slot ranges, laid end to end in unit order, form
+// one sequence of `total` slots, cut into equal segments of S = max(ceil(total / P),
 // split) tokens, P being the number of workgroups that fit on the device at once, or half
 // of them when total / P is below kShortSegment tokens or when the half grid's segments
 // cut no unit and the full grid's would.  The grid holds the resident
 // workgroups; workgroup s streams segment s, which may
 // cover the end of one unit, whole units, and the start of another.  Every workgroup
-// first scans all units (selected-token count N_u from seq_lens, sel_cnt and the last
-// selected block) for the prefix sums; that costs a few dependent loads once per
-// workgroup instead of once per chunk, and equal segments leave no tail of late chunks
-// and no imbalance between XCDs.  A unit that lies inside one segment is finished by
+// first scans all units (N_u from sel_cnt and the block size: one round of independent
+// loads, no dependent read of the list) for the prefix sums; that costs a load round
+// once per workgroup instead of once per chunk, and equal segments leave no tail of late
+// chunks and no imbalance between XCDs.  A unit that lies inside one segment is finished by
 // that workgroup.  A unit that crosses segment boundaries leaves one partial (o, m, l)
 // per segment it touches: in its first segment in slot 1 ("tail") of that segment, in
 // later ones in slot 0 ("head"); its first segment also records (unit, piece count).
-// Units with no tokens (N_u = 0) get out = 0 and lse = -inf from workgroup u mod (grid size).
+// Units with no selected block (N_u = 0) get out = 0 and lse = -inf from workgroup
+// u mod (grid size); a unit whose slots are all masked gets the same from its merge (l = 0).
 //
 // k_decode (4 waves per workgroup): within a piece of a unit, tokens go through LDS
 // lists of at most kMaxSplit tokens' block indices; each list is shared out to the four
@@ -188,18 +190,20 @@ __device__ __forceinline__ void pv_pair(const uint32_t* pk, const uint4& va, con
 }
 
 
-// Selected-token count of unit u: N = (cnt - 1) * g + the valid tokens of the last
-// selected block (0 when cnt == 0).  seq_lens and sel_cnt outside their ranges are
-// clamped and, when `report`, flagged.
+// Sequence length and token slots of unit u: N = cnt * g (the masked tail of a partial
+// last block included, so no entry of the list has to be read first).  seq_lens and
+// sel_cnt outside their ranges are clamped and, when `report`, flagged; a count above the
+// unit's n_cap block slots cannot be a valid list (FX_ERR_SEL_INDEX) and is clamped to it,
+// which bounds the slots of all units below 2^31 (checked at plan creation).
 struct UnitTokens {
   int T, N;
 };
 
 __device__ __forceinline__ UnitTokens unit_tokens(const UnitInfo* units, const int32_t* seq_lens,
-                                                  const int32_t* sel_idx, const int32_t* sel_cnt,
-                                                  int u, int Hkv, int t_cap, int max_sel,
-                                                  bool report, uint32_t* err) {
-  const int g = units[u].g;
+                                                  const int32_t* sel_cnt, int u, int Hkv,
+                                                  int t_cap, int max_sel, bool report,
+                                                  uint32_t* err) {
+  const int g = units[u].g, n_cap = units[u].n_cap;
   int T = seq_lens[u / Hkv];
   int cnt = sel_cnt[u];
   if (T < 0 || T > t_cap) {
@@ -210,13 +214,11 @@ __device__ __forceinline__ UnitTokens unit_tokens(const UnitInfo* units, const i
     if (report) atomicOr(err, (uint32_t)FX_ERR_SEL_COUNT);
     cnt = cnt < 0 ? 0 : max_sel;
   }
-  int N = 0;
-  if (cnt > 0) {
-    const int64_t last = sel_idx[(size_t)u * max_sel + cnt - 1];
-    const int64_t valid_last = min(max((int64_t)T - last * g, (int64_t)0), (int64_t)g);
-    N = (cnt - 1) * g + (int)valid_last;
+  if (cnt > n_cap) {
+    if (report) atomicOr(err, (uint32_t)FX_ERR_SEL_INDEX);
+    cnt = n_cap;
   }
-  return {T, N};
+  return {T, cnt * g};
 }
 
 template <typename E, int D, int G, bool ED>
@@ -303,8 +305,8 @@ __global__ __launch_bounds__(NT, 2) void k_decode(
 #pragma unroll
     for (int k = 0; k < kScanKeep; ++k) {
       const int u = c0 + k * NT + (int)threadIdx.x;
-      Nk[k] = u < n_units ? unit_tokens(units, seq_lens, sel_idx, sel_cnt, u, Hkv, t_cap, max_sel,
-                                        seg == 0, err).N
+      Nk[k] = u < n_units ? unit_tokens(units, seq_lens, sel_cnt, u, Hkv, t_cap, max_sel, seg == 0,
+                                        err).N
                           : 0;
     }
 #pragma unroll
@@ -356,7 +358,7 @@ __global__ __launch_bounds__(NT, 2) void k_decode(
 #pragma unroll
       for (int k = 0; k < kScanKeep; ++k) N = (c0 == k * NT) ? keepN[k] : N;
     } else if (u < n_units) {
-      N = unit_tokens(units, seq_lens, sel_idx, sel_cnt, u, Hkv, t_cap, max_sel, false, err).N;
+      N = unit_tokens(units, seq_lens, sel_cnt, u, Hkv, t_cap, max_sel, false, err).N;
     }
     int chunk_total;
     const int incl = running + block_incl_scan(N, L.scan[(it + 1) & 1], &chunk_total);
@@ -432,8 +434,7 @@ __global__ __launch_bounds__(NT, 2) void k_decode(
   bool recorded = false;
   int cur = s0;
   while (cur < s1) {
-    const UnitTokens ut =
-        unit_tokens(units, seq_lens, sel_idx, sel_cnt, u, Hkv, t_cap, max_sel, false, err);
+    const UnitTokens ut = unit_tokens(units, seq_lens, sel_cnt, u, Hkv, t_cap, max_sel, false, err);
     const int N = ut.N;
     if (N == 0) {
       ++u;

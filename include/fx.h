@@ -185,9 +185,10 @@ typedef struct fx_plan* fx_plan_t;
 
 /* Validate the shapes and the per-unit policies (host array of B*Hkv entries,
  * copied), compute the packed layouts, and allocate the plan's device table on
- * the current HIP device; the decode split is sized for that device.  The most
- * tokens all units can select together, sum over u of min(max_sel(u) * block(u),
- * t_cap), must stay below 2^31 (else FX_E_UNSUPPORTED).  *out is set only on FX_OK. */
+ * the current HIP device; the decode split is sized for that device.  The token slots
+ * of the longest valid selection lists, sum over u of min(n_cap(u), max_sel) * block(u)
+ * (n_cap(u) = ceil(t_cap / block(u)), max_sel the lists' row stride), must stay below
+ * 2^31 (else FX_E_UNSUPPORTED).  *out is set only on FX_OK. */
 fx_status fx_plan_create(const fx_plan_desc* desc, const fx_head_policy* host_policies,
                          fx_plan_t* out);
 /* Free the plan's device table.  NULL is a no-op.  Waits for nothing: the caller
@@ -292,9 +293,11 @@ fx_status fx_select_delta(fx_plan_t plan, const void* q, const void* summaries,
  * For each unit and each of its G query rows q: over the valid tokens t of the
  * selected blocks, s_t = softmax_scale * (q . K_t); out = sum_t e^{s_t - m} V_t / l
  * with m = max s_t and l = sum_t e^{s_t - m}; lse = m + ln l.  Computed as
- * flash-decoding with a float32 online softmax: the units' selected tokens, laid end
- * to end, are cut into as many equal segments (at least split_tokens long) as the
- * GPU holds decode workgroups at once, one per workgroup; a unit cut by a segment
+ * flash-decoding with a float32 online softmax: the token slots of the units' selected
+ * blocks (block(u) per selected block; slots past the sequence end or in an invalid
+ * entry are masked and read no memory), laid end to end, are cut into as many equal
+ * segments (at least split_tokens long) as the GPU holds decode workgroups at once, one
+ * per workgroup; a unit cut by a segment
  * boundary is finished by a log-sum-exp merge of its pieces in a second kernel, in
  * piece order.  Results depend only on the inputs and the plan (on one device), not
  * on scheduling.  A unit with no valid token gets out = 0, lse = -inf.
