@@ -53,7 +53,9 @@
 // steps where some running max grew.  For bfloat16 the P.V update takes tokens in pairs:
 // p is rounded to bfloat16, paired within the quad, broadcast along the row (DPP
 // row_newbcast), and one v_dot2_f32_bf16 per (row, column) accumulates both tokens.
-// Lane groups, then waves, merge with the log-sum-exp rule.
+// The lane groups of a wave merge down to as many as fit in its LDS area, those publish
+// their partial (o, m, l), and the workgroup merges them with the log-sum-exp rule in a
+// fixed order.
 //
 // k_combine (one workgroup per segment, exits unless the segment recorded a unit that
 // continues past it) merges that unit's partials in segment order with the
@@ -224,18 +226,29 @@ __device__ __forceinline__ UnitTokens unit_tokens(const UnitInfo* units, const i
 template <typename E, int D, int G, bool ED>
 struct DecodeLds {
   using SL = Slots<E, D, G>;
+  // Lane groups per wave whose (o, m, l) go to LDS at the end of a piece: as many as fit in
+  // the wave's slot area (a power of two); the others are first merged into them in
+  // registers.
+  static constexpr int keep_groups() {
+    int k = 64 / SL::LPT;
+    while (k > 1 && k * G * D > (64 / SL::LPT) * SL::GS) k /= 2;
+    return k;
+  }
+  static constexpr int KEEP = keep_groups();
+  static constexpr int NG = NWAVES * KEEP;        // partials merged by the workgroup
   // Per wave: its lane groups' partial dot products during the token steps, then, after
-  // the wave's last step of a piece, its (o) of the query rows.  Only the wave itself
-  // writes its area; a barrier separates the merge's reads from the next piece's steps.
+  // the wave's last step of a piece, KEEP lane groups' (o) of the query rows.  Only the
+  // wave itself writes its area; a barrier separates the merge's reads from the next
+  // piece's steps.
   union WaveArea {
     float tr[64 / SL::LPT][SL::GS];
-    float o[G][D];
+    float og[KEEP][G][D];
   };
   alignas(16) WaveArea wa[NWAVES];
   int blk[kMaxSplit + 1];          // selected block indices of the current token run
   float bias[ED ? kMaxSplit + 1 : 1];   // their eviction logits times log2(e) (ED only)
-  float m[NWAVES][G];
-  float l[NWAVES][G];
+  float m[NG][G];                  // each lane group's running max and sum per query row
+  float l[NG][G];
   int scan[2][NWAVES];
   int scan2[2][NWAVES];
   int first_unit, first_pos;       // the unit holding the segment's first token (full grid)
@@ -667,9 +680,15 @@ __global__ __launch_bounds__(NT, 2) void k_decode(
         lf[gg] = group_bcast<LPT, (gg % QPR) * U>(lq[gg / QPR]);
       });
     }
-    // Merge the lane groups of the wave (partners differ in the lane bits above LPT).
+    // Merge the lane groups of the wave down to KEEP (partners differ in the lane bits
+    // from LPT * KEEP up).  Those publish their (o, m, l); after the barrier the workgroup
+    // merges all NG of them in (wave, group) order, four columns per thread.  Merging all
+    // the lane groups in registers took a chain of cross-lane shuffles per query row
+    // (1.7 us per wave with seven rows and four groups), every wave of the workgroup then
+    // waiting at the barrier.
+    constexpr int KEEP = DecodeLds<E, D, G, ED>::KEEP;
 #pragma unroll
-    for (int off = LPT; off < 64; off <<= 1) {
+    for (int off = LPT * KEEP; off < 64; off <<= 1) {
 #pragma unroll
       for (int gg = 0; gg < G; ++gg) {
         const float m2 = __shfl_xor(mf[gg], off);
@@ -686,40 +705,55 @@ __global__ __launch_bounds__(NT, 2) void k_decode(
         mf[gg] = M;
       }
     }
-    if (lg == 0) {
+    if (lg < KEEP) {
+      float* og = &L.wa[wave].og[lg][0][0];
 #pragma unroll
-      for (int gg = 0; gg < G; ++gg) {
+      for (int gg = 0; gg < G; ++gg)
 #pragma unroll
-        for (int z = 0; z < EPL; ++z) L.wa[wave].o[gg][li * EPL + z] = o[gg][z];
-        if (li == 0) {
-          L.m[wave][gg] = mf[gg];
-          L.l[wave][gg] = lf[gg];
+        for (int z = 0; z < EPL; z += 4)
+          *reinterpret_cast<float4*>(og + gg * D + li * EPL + z) =
+              make_float4(o[gg][z], o[gg][z + 1], o[gg][z + 2], o[gg][z + 3]);
+      if (li == 0) {
+#pragma unroll
+        for (int gg = 0; gg < G; ++gg) {
+          L.m[wave * KEEP + lg][gg] = mf[gg];
+          L.l[wave * KEEP + lg][gg] = lf[gg];
         }
       }
     }
     __syncthreads();
 
-    // Merge the waves in wave order; then finish the unit or publish a partial.
+    // Finish the unit or publish a partial.
     const bool whole = a == 0 && e == N;
     const size_t pbase = (size_t)seg * 2 + (a == 0 ? 1 : 0);
-    for (int idx = threadIdx.x; idx < G * D; idx += NT) {
-      const int gg = idx / D, c = idx % D;
+    for (int idx = threadIdx.x; idx < G * D / 4; idx += NT) {
+      constexpr int NG = DecodeLds<E, D, G, ED>::NG;
+      const int gg = idx / (D / 4), c = (idx % (D / 4)) * 4;
       float M = L.m[0][gg];
 #pragma unroll
-      for (int w = 1; w < NWAVES; ++w) M = fmaxf(M, L.m[w][gg]);
-      float Ls = 0.0f, Os = 0.0f;
+      for (int k = 1; k < NG; ++k) M = fmaxf(M, L.m[k][gg]);
+      float Ls = 0.0f;
+      float4 Os = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
 #pragma unroll
-      for (int w = 0; w < NWAVES; ++w) {
-        const float x = __builtin_amdgcn_exp2f(L.m[w][gg] - M);
-        Ls = fmaf(L.l[w][gg], x, Ls);
-        Os = fmaf(L.wa[w].o[gg][c], x, Os);
+      for (int k = 0; k < NG; ++k) {
+        const float x = __builtin_amdgcn_exp2f(L.m[k][gg] - M);
+        const float4 ov = *reinterpret_cast<const float4*>(&L.wa[k / KEEP].og[k % KEEP][gg][c]);
+        Ls = fmaf(L.l[k][gg], x, Ls);
+        Os.x = fmaf(ov.x, x, Os.x);
+        Os.y = fmaf(ov.y, x, Os.y);
+        Os.z = fmaf(ov.z, x, Os.z);
+        Os.w = fmaf(ov.w, x, Os.w);
       }
       if (whole) {
         const size_t orow = (size_t)b * Hkv * G + (size_t)h * G + gg;
-        store_elem(out + orow * D + c, Ls > 0.0f ? Os / Ls : 0.0f);
+        E* dst = out + orow * D + c;
+        store_elem(dst + 0, Ls > 0.0f ? Os.x / Ls : 0.0f);
+        store_elem(dst + 1, Ls > 0.0f ? Os.y / Ls : 0.0f);
+        store_elem(dst + 2, Ls > 0.0f ? Os.z / Ls : 0.0f);
+        store_elem(dst + 3, Ls > 0.0f ? Os.w / Ls : 0.0f);
         if (lse && c == 0) lse[orow] = Ls > 0.0f ? (M + __log2f(Ls)) * kLn2 : -__builtin_inff();
       } else {
-        part_o[(pbase * G + gg) * D + c] = Os;
+        *reinterpret_cast<float4*>(&part_o[(pbase * G + gg) * D + c]) = Os;
         if (c == 0) part_ml[pbase * G + gg] = make_float2(M, Ls);
       }
     }
