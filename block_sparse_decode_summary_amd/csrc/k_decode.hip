@@ -251,6 +251,7 @@ struct DecodeLds {
   float l[NG][G];
   int scan[2][NWAVES];
   int scan2[2][NWAVES];
+  int cuts[NWAVES];                // per wave: bit 0 the full grid, bit 1 the half grid cuts a unit
   int first_unit, first_pos;       // the unit holding the segment's first token (full grid)
   int first_unit_h, first_pos_h;   // the same on the half grid
   int unit_a, pos_a, piece_a, pieces_a, n_a;   // unit-aligned segments: unit, its first
@@ -405,8 +406,20 @@ __global__ __launch_bounds__(NT, 2) void k_decode(
     }
     running += chunk_total;
   }
-  cut_f = __syncthreads_or(cut_f);
-  cut_h = __syncthreads_or(cut_h);
+  // One barrier publishes both cut flags and the scan's first-unit records.
+  {
+    const uint64_t bf = __builtin_amdgcn_ballot_w64(cut_f);
+    const uint64_t bh = __builtin_amdgcn_ballot_w64(cut_h);
+    if (lane == 0) L.cuts[wave] = (bf != 0 ? 1 : 0) | (bh != 0 ? 2 : 0);
+  }
+  __syncthreads();
+  {
+    int cw = 0;
+#pragma unroll
+    for (int i = 0; i < NWAVES; ++i) cw |= L.cuts[i];
+    cut_f = (cw & 1) != 0;
+    cut_h = (cw & 2) != 0;
+  }
   const bool half = short_full || (can_half && cut_f && !cut_h);
   const int S = half ? Sh : Sf;
   const int nseg = aligned ? pieces : (total + S - 1) / S;
@@ -414,7 +427,6 @@ __global__ __launch_bounds__(NT, 2) void k_decode(
     if (threadIdx.x == 0) seg_rec[seg] = make_int2(-1, 0);
     return;
   }
-  __syncthreads();
   int s0 = half ? s0h : s0f, s1 = min(s0 + S, total);
   int u = __builtin_amdgcn_readfirstlane(half ? L.first_unit_h : L.first_unit);
   int Pu = __builtin_amdgcn_readfirstlane(half ? L.first_pos_h : L.first_pos);
