@@ -154,6 +154,22 @@ def test_ragged_degenerate_lengths_and_mixed_modes():
         _run_and_compare_all(w.replace(name=f"ragged_mixed_{n_cap}", t_cap=n_cap * 16), steps=1)
 
 
+def test_segments_of_masked_slots_only():
+    """The decode partitions token slots (selected blocks times the block size), so the tail
+    of a partial last block counts as slots that read nothing.  With blocks of 128 tokens,
+    lengths of the form 128 k + 1 and 64-slot segments, some segments hold only masked
+    slots: every unit against the oracle, with few units (each unit cut into its own pieces)
+    and with more units (stream-K across units), at 64-slot segments and the default."""
+    lens_cycle = [1, 127, 128, 129, 255, 257, 385, 1025]
+    pol_s = HeadPolicy(MODE_STREAMING, block=128, sub_block=128, sink_tokens=1, local_tokens=100000)
+    pol_r = HeadPolicy(MODE_RETRIEVAL, block=128, sub_block=32, top_k=4, force_sink=1, force_last=1)
+    for B in (4, 20):
+        lens = [lens_cycle[i % len(lens_cycle)] for i in range(B)]
+        w = _custom(f"masked_slots_b{B}", B, 4, 2, 64, "bf16", 1152, lens, [pol_s, pol_r] * B)
+        _run_and_compare_all(w.replace(name=f"masked_slots_b{B}_s64"), split_tokens=64)
+        _run_and_compare_all(w)
+
+
 def test_more_units_than_one_scan_chunk():
     """2080 units (three chunks of the decode's unit scan, which keeps 1024 units in
     registers), ragged short lengths with empty units, all three modes: every unit against
