@@ -220,6 +220,26 @@ fx_status plan_create(const fx_plan_desc* desc, const fx_head_policy* pol, fx_pl
     delete p;
     return FX_E_HIP;
   }
+  // With the automatic split, plans whose units all fit a short piece keep every unit
+  // whole: the decode cuts each unit into its own pieces (few units on a large grid, the
+  // kernel's unit-aligned rule), each at least decode_split slots long, so a minimum as
+  // large as the longest possible unit leaves one piece per unit and nothing to merge.
+  // A second kernel's launch and round trips cost more than streaming such a unit in
+  // one workgroup (the tiny workload's 320-slot units).
+  p->decode_split = p->split;
+  {
+    int64_t max_unit_slots = 0;
+    for (const UnitInfo& ui : p->host_units)
+      max_unit_slots = std::max<int64_t>(max_unit_slots, std::min<int64_t>(ui.n_cap, max_sel) * ui.g);
+    auto aligned_on = [&](int grid) {
+      return grid >= 2 * fx::kCUsMin && (int64_t)units * fx::kAlignedUnitsDiv <= grid / 2;
+    };
+    if (desc->split_tokens == 0 && max_unit_slots <= fx::kUncutSlots &&
+        aligned_on(p->decode_grid) && aligned_on(p->decode_grid_ed)) {
+      p->decode_uncut = true;
+      p->decode_split = std::max<int32_t>(p->split, (int32_t)max_unit_slots);
+    }
+  }
 
   const int d = desc->head_dim;
   size_t off = 0;

@@ -21,6 +21,8 @@ constexpr int kMinSplit = 64;
 constexpr int kAutoSplit = 256;       // minimum decode segment when the caller passes 0
 constexpr int kShortSegment = 1024;   // below this many tokens per segment, use half the grid
 constexpr int kCUsMin = 64;           // (only on grids of at least 2 * kCUsMin workgroups)
+constexpr int kAlignedUnitsDiv = 8;   // unit-aligned decode pieces when units <= half grid / this
+constexpr int kUncutSlots = 512;      // auto split: units of at most this many token slots stay whole
 constexpr uint64_t kStreamReadSpan = 1ull << 20;   // bytes per workgroup of fx_stream_read
 constexpr int kMaxTcap = 1 << 24;
 constexpr int kTopkRegBlocks = 8192;   // selection keeps keys in registers up to this n_cap
@@ -91,6 +93,8 @@ struct fx_plan {
   int32_t max_n_cap = 0;
   int32_t max_n_full_cap = 0;    // max over units of t_cap / g
   int32_t split = 0;             // minimum decode segment in tokens (power of two)
+  int32_t decode_split = 0;      // the minimum segment the decode kernel uses (>= split)
+  bool decode_uncut = false;     // no unit can be cut into pieces: no merge kernel
   int32_t decode_grid = 0;       // decode workgroups = decode segments
   int32_t decode_grid_ed = 0;    // the same for fx_sparse_decode_ed (<= decode_grid)
   bool any_scored = false;       // some unit is retrieval or NOSA

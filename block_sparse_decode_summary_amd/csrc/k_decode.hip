@@ -19,8 +19,8 @@
 //
 // Work split (stream-K): the units' slot ranges, laid end to end in unit order, form
 // one sequence of `total` slots, cut into equal segments of S = max(ceil(total / P),
-// split) tokens, P being the number of workgroups that fit on the device at once, or half
-// of them when total / P is below kShortSegment tokens or when the half grid's segments
+// split) slots, P being the number of workgroups that fit on the device at once, or half
+// of them when total / P is below kShortSegment slots or when the half grid's segments
 // cut no unit and the full grid's would.  The grid holds the resident
 // workgroups; workgroup s streams segment s, which may
 // cover the end of one unit, whole units, and the start of another.  Every workgroup
@@ -259,7 +259,6 @@ struct DecodeLds {
 };
 
 constexpr int kScanKeep = 4;       // unit chunks (NT units each) kept in registers between scans
-constexpr int kAlignedUnitsDiv = 8; // unit-aligned segments when units <= half grid / this
 
 // Inclusive prefix sum over the workgroup (slot: NWAVES ints, written then read after one
 // barrier; alternate slots between consecutive calls).
@@ -859,14 +858,14 @@ int launch_t(const fx_plan* p, const void* q, const void* K, const void* V,
         p->d_units, static_cast<const E*>(q), static_cast<const E*>(K),
         static_cast<const E*>(V), seq_lens, sel_idx, sel_cnt, logits, softmax_scale * kLog2e,
         static_cast<E*>(out), lse, part_o, part_ml, seg_rec, p->d_error, Hkv, t_cap, p->max_sel,
-        p->units, p->split);
+        p->units, p->decode_split);
   };
   if (logits)
     args(k_decode<E, D, G, kU, true>);
   else
     args(k_decode<E, D, G, kU, false>);
   const int e = hipGetLastError();
-  if (e != 0) return e;
+  if (e != 0 || p->decode_uncut) return e;   // uncut plans finish every unit in place
   // One thread per output (query row, column).
   constexpr int kCombineThreads = G * D < 1024 ? G * D : 1024;
   k_combine<E, D, G><<<grid, kCombineThreads, 0, stream>>>(
