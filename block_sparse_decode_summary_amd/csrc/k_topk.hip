@@ -30,8 +30,8 @@
 // them with lane broadcasts.
 //
 // Mapping: one NT-thread workgroup per unit (NT = 256; 512 for the selection that forms
-// its own scores when units have 257-512 block slots; 1024 for plans with few units and
-// more than 1024 block slots).  Thread t owns blocks j = i*NT + t.  When every
+// its own scores when units have 257-512 block slots, and for plans of many units with
+// 1025-4096 block slots; 1024 for plans with few units and more than 1024 block slots).  Thread t owns blocks j = i*NT + t.  When every
 // unit has at most 8192 block slots the keys, the candidate flags and the old eviction
 // words stay in registers (k_topk_reg), wave ballots of the per-block flags give the
 // bitmap words, and a scan over (row, wave) counts compacts the selection straight into
@@ -150,6 +150,17 @@ int launch_topk(const fx_plan* p, const float* scores, const float* logits, uint
     // The workspace path leaves the differences to the delta kernel.
     return launch_delta(p, prev_idx, prev_cnt, sel_idx, sel_cnt, added, added_cnt, removed,
                         removed_cnt, stream);
+  }
+  if (p->units >= kFewUnits && n > 2 * topk512::NT && n <= 8 * topk512::NT) {
+    // 1025-4096 block slots: 512 threads per unit (4 or 8 blocks per thread) halve the
+    // per-thread serial parts of the k-th search against 256 (mixed_serving, 2048 slots:
+    // k_topk_reg 8.1 against 9.0 us).
+    const topk512::DeltaArgs D{prev_idx, prev_cnt, added, added_cnt, removed, removed_cnt};
+    if (n <= 4 * topk512::NT)
+      topk512::launch_reg<4>(p, scores, logits, mask, seq_lens, sel_idx, sel_cnt, D, stream);
+    else
+      topk512::launch_reg<8>(p, scores, logits, mask, seq_lens, sel_idx, sel_cnt, D, stream);
+    return hipGetLastError();
   }
   if (p->units < kFewUnits && n > topk1024::NT) {
     const topk1024::DeltaArgs D{prev_idx, prev_cnt, added, added_cnt, removed, removed_cnt};

@@ -6,8 +6,9 @@ fx_sparse_decode as in a bench step).  For every unit: summaries, float32 scores
 selections, -1 padding and the differences bit-exact; out and lse within the decode
 tolerances; for NOSA units the eviction mask bit-exact and the locality bound
 |cur & prev| / |cur| >= k_e / k every step.  nosa_drift runs all 64 drift steps this way.
-Two plans of 128 units with 2049-4096 and 4097-8192 block slots run the 256-thread
-register selections with 16 and 32 blocks per thread.
+Two plans of 128 units with 2049-4096 and 4097-8192 block slots run the register
+selections with 512 threads and 8 blocks per thread, and with 256 threads and 32 blocks
+per thread.
 
 The oracle runs on the host in a thread pool (NumPy releases the interpreter lock in
 its array work; one BLAS thread per call).  The largest ratio of error to allowed error
@@ -215,7 +216,7 @@ def _wide_plan_workload(n_cap: int) -> Workload:
 
 
 @pytest.mark.parametrize("n_cap", [3000, 6000])
-def test_register_selection_16_and_32_blocks_per_thread(n_cap):
+def test_register_selection_of_wide_units(n_cap):
     w = _wide_plan_workload(n_cap)
     plan = make_plan(w)
     assert plan.units >= 128
