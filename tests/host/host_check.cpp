@@ -423,11 +423,50 @@ static void test_other_calls() {
   CHECK(std::strstr(fx_status_string(42), "unknown") != nullptr);
 }
 
+// The automatic split keeps every unit whole (and the decode launches no merge kernel)
+// only when the decode cuts units into their own pieces (at most half grid / 8 units on
+// a grid of at least 128 workgroups) and no unit can hold more than 512 token slots.
+static void test_uncut_plans() {
+  fx_plan_t plan = nullptr;
+  // Two units of at most 10 blocks of 32 tokens: 320 slots.
+  fx_plan_desc d = desc(1, 4, 2, 64, 2048, FX_F32);
+  fx_head_policy small[2] = {retrieval(32, 8), retrieval(32, 8)};
+  CHECK(fx_plan_create(&d, small, &plan) == FX_OK);
+  CHECK(plan->decode_uncut && plan->decode_split == 320);
+  CHECK(fx_split_tokens(plan) == 256);
+  CHECK(fx_plan_destroy(plan) == FX_OK);
+  // An explicit split is kept as given.
+  d.split_tokens = 128;
+  CHECK(fx_plan_create(&d, small, &plan) == FX_OK);
+  CHECK(!plan->decode_uncut && plan->decode_split == 128);
+  CHECK(fx_plan_destroy(plan) == FX_OK);
+  d.split_tokens = 0;
+  // Units of up to 28 blocks of 64 tokens (1792 slots) are cut into pieces.
+  fx_plan_desc d8 = desc(1, 32, 8, 128, 32768, FX_BF16);
+  std::vector<fx_head_policy> big(8, retrieval(64, 26));
+  CHECK(fx_plan_create(&d8, big.data(), &plan) == FX_OK);
+  CHECK(!plan->decode_uncut && plan->decode_split == 256);
+  CHECK(fx_plan_destroy(plan) == FX_OK);
+  // 40 small units on a 512-workgroup grid: more than 256 / 8, so stream-K, which may cut.
+  fx_plan_desc d40 = desc(20, 4, 2, 64, 2048, FX_F32);
+  std::vector<fx_head_policy> many(40, retrieval(32, 8));
+  CHECK(fx_plan_create(&d40, many.data(), &plan) == FX_OK);
+  CHECK(!plan->decode_uncut);
+  CHECK(fx_plan_destroy(plan) == FX_OK);
+  // A grid below 128 workgroups has no half grid and no unit-aligned pieces.
+  stub::decode_grid = 100;
+  CHECK(fx_plan_create(&d, small, &plan) == FX_OK);
+  CHECK(!plan->decode_uncut && plan->decode_split == 256);
+  CHECK(fx_plan_destroy(plan) == FX_OK);
+  stub::decode_grid = 512;
+}
+
 int main() {
   test_descriptions();
   test_policies();
   test_layout_and_sizes();
   test_create_failures();
+  test_uncut_plans();
   test_select();
   test_decode();
   test_other_calls();
