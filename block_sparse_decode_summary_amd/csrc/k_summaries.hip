@@ -74,7 +74,7 @@ __global__ __launch_bounds__(256) void k_build_summaries(
     double acc[EPW];
 #pragma unroll
     for (int e = 0; e < EPW; ++e) acc[e] = 0.0;
-#pragma unroll 8
+#pragma unroll 16   // a sub-block of 16 rows in one round of loads (nosa_drift: 5.1 -> 4.5 us)
     for (int r = 0; r < s; ++r) {
       double v[EPW];
       widen(p[(size_t)r * WORDS], v, (E*)nullptr);
