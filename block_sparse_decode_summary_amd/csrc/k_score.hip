@@ -185,7 +185,11 @@ __global__ __launch_bounds__(NW * 64) void k_score_sum(
   uint4* const qrows = sh.qrows;
   __shared__ double qs[D];
   const int n_su = gridDim.x / quads_per_unit;
-  const int quad = blockIdx.x / n_su;
+  // One-tile grids run the highest tile indices first: the workgroups past a short unit's
+  // end (most of them are at high indices) then come and go while slots are still free,
+  // instead of among the last tiles, which wait for slots (mixed_serving k_score_sum 19.8
+  // against 20.3 us).
+  const int quad = NW == 1 ? quads_per_unit - 1 - (int)(blockIdx.x / n_su) : (int)(blockIdx.x / n_su);
   const int su = blockIdx.x % n_su;
   const int u = scored[su];
   const UnitInfo ui = units[u];
