@@ -360,8 +360,9 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU (asked for --gpus {args.gpus}); "
-              f"the path shards by (sequence, kv head) with no exchange, see DESIGN.md",
+        print(f"bench.py: the benchmark runs on exactly one GPU (asked for --gpus {args.gpus}); "
+              f"units (sequence, kv head) are independent, so each GPU would run the same calls "
+              f"on its own share of sequences or kv heads with no exchange",
               file=sys.stderr)
         return 2
 

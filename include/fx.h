@@ -98,7 +98,7 @@ typedef int32_t fx_status;
 enum {
   FX_OK = 0,
   FX_E_INVALID = 1,       /* an argument or policy is out of range, null or misaligned */
-  FX_E_UNSUPPORTED = 2,   /* a valid request this build has no kernel for */
+  FX_E_UNSUPPORTED = 2,   /* a valid request the library has no kernel for */
   FX_E_WORKSPACE = 3,     /* workspace smaller than fx_workspace_bytes() */
   FX_E_HIP = 4            /* a HIP runtime call or kernel launch failed */
 };

@@ -4,7 +4,7 @@ This package only describes shapes and draws inputs. It holds none of the
 method's arithmetic (no pooling, scoring, selection or attention): the HIP
 library and the CPU oracle both receive exactly the tensors built here.
 
-Workloads follow the five shapes this build is measured on:
+Workloads follow five benchmark shapes:
 
   tiny            1 seq, 4 q / 2 kv heads, d 64, fp32, context 2048, block 32
   llama8b_layer   1 seq, 32 / 8, d 128, bf16, context 32768, block 64,
